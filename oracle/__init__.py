@@ -1,0 +1,189 @@
+"""CPU oracle of the bit-exact tile-MMA emulation -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, the smoke check and the benchmark's ``cpu_baseline`` leg
+may import this package.  It wraps ``liboracle.so`` (plain C, built from
+``mma_oracle.c`` with gcc) through ctypes, taking and returning numpy arrays
+of raw bit patterns.  It shares no code with the HIP library.
+
+The arithmetic it follows is the Hawkeye recovered MMA model ("Hawkeye:
+Reproducing GPU-Level Non-Determinism (MLSys 2026)" reading notes, sections
+"Key observations" and "Recovered Ampere FP16 pipeline"); each rule is stated
+and cited at the top of ``mma_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "mma_oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+AMPERE, HOPPER = 0, 1
+FP16, BF16, E4M3 = 0, 1, 2
+
+MODELS = {"ampere": AMPERE, "hopper": HOPPER}
+DTYPES = {"fp16": FP16, "bf16": BF16, "e4m3": E4M3}
+CODE_DTYPE = {FP16: np.uint16, BF16: np.uint16, E4M3: np.uint8}
+
+
+def build(force: bool = True) -> str:
+    """Compile liboracle.so with gcc (plain C99 + pthreads)."""
+    if force or not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        tmp = LIB + ".tmp"
+        cmd = ["gcc", "-std=c99", "-D_DEFAULT_SOURCE", "-O2", "-fPIC", "-shared",
+               "-Wall", "-Wextra", "-pthread", SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, LIB)
+    return LIB
+
+
+_lib = None
+
+
+def _bind(lib):
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.mma_oracle_gemm.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, i32]
+    lib.mma_oracle_gemm_rows.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64,
+                                         i64, i64, vp, i32]
+    lib.mma_oracle_tiles.argtypes = [i32, i32, vp, vp, vp, vp, i64, vp, i32]
+    lib.mma_oracle_dots.argtypes = [i32, i32, vp, vp, vp, vp, i64]
+    lib.mma_oracle_num_cpus.argtypes = []
+    for f in (lib.mma_oracle_gemm, lib.mma_oracle_gemm_rows, lib.mma_oracle_tiles,
+              lib.mma_oracle_dots, lib.mma_oracle_num_cpus):
+        f.restype = i32
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build(force=False)
+        _lib = _bind(ctypes.CDLL(LIB))
+    return _lib
+
+
+def _enum(v, table):
+    return table[v] if isinstance(v, str) else int(v)
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _codes(x, dtype):
+    x = np.ascontiguousarray(x)
+    want = CODE_DTYPE[dtype]
+    if x.dtype != want:
+        raise TypeError(f"expected {np.dtype(want).name} codes, got {x.dtype}")
+    return x
+
+
+def _bits32(x):
+    if x is None:
+        return None
+    x = np.ascontiguousarray(x)
+    if x.dtype == np.float32:
+        x = x.view(np.uint32)
+    if x.dtype != np.uint32:
+        raise TypeError(f"expected uint32/float32 bit patterns, got {x.dtype}")
+    return x
+
+
+def _check(rc, what):
+    if rc != 0:
+        raise ValueError(f"{what} rejected its arguments (code {rc})")
+
+
+def num_cpus() -> int:
+    return _load().mma_oracle_num_cpus()
+
+
+def gemm(model, dtype, A, B, C=None, nthreads=0, xorsum=True, lib=None):
+    """D (uint32 bits, M x N) and per-row xorsum (or None) of the emulated GEMM."""
+    lib = lib or _load()
+    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    A, B, C = _codes(A, d), _codes(B, d), _bits32(C)
+    M, K = A.shape
+    K2, N = B.shape
+    assert K == K2 and (C is None or C.shape == (M, N))
+    D = np.empty((M, N), np.uint32)
+    x = np.empty(M, np.uint32) if xorsum else None
+    _check(lib.mma_oracle_gemm(m, d, _ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K,
+                                   _ptr(x), int(nthreads)), "mma_oracle_gemm")
+    return D, x
+
+
+def gemm_rows(model, dtype, A, B, C, row_begin, row_end, nthreads=0, lib=None):
+    """Rows [row_begin, row_end) of D and their xorsums."""
+    lib = lib or _load()
+    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    A, B, C = _codes(A, d), _codes(B, d), _bits32(C)
+    M, K = A.shape
+    N = B.shape[1]
+    rows = row_end - row_begin
+    D = np.empty((rows, N), np.uint32)
+    x = np.empty(rows, np.uint32)
+    _check(lib.mma_oracle_gemm_rows(m, d, _ptr(A), _ptr(B), _ptr(C), _ptr(D), M, N, K,
+                                        row_begin, row_end, _ptr(x), int(nthreads)),
+           "mma_oracle_gemm_rows")
+    return D, x
+
+
+def tiles(model, dtype, A, B, C=None, nthreads=0, lib=None):
+    """D and per-tile xorsum of ntiles independent 16x16x16 MMAs."""
+    lib = lib or _load()
+    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    A, B, C = _codes(A, d), _codes(B, d), _bits32(C)
+    n = A.shape[0]
+    assert A.shape == (n, 16, 16) and B.shape == (n, 16, 16)
+    D = np.empty((n, 16, 16), np.uint32)
+    x = np.empty(n, np.uint32)
+    _check(lib.mma_oracle_tiles(m, d, _ptr(A), _ptr(B), _ptr(C), _ptr(D), n, _ptr(x),
+                                    int(nthreads)), "mma_oracle_tiles")
+    return D, x
+
+
+def dots(model, dtype, a, b, c, lib=None):
+    """d[r] = one MMA step for a single output: c[r] + sum_k a[r,k] b[r,k]."""
+    lib = lib or _load()
+    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    a, b, c = _codes(a, d), _codes(b, d), _bits32(c)
+    n = a.shape[0]
+    assert a.shape == (n, 16) and b.shape == (n, 16) and c.shape == (n,)
+    out = np.empty(n, np.uint32)
+    _check(lib.mma_oracle_dots(m, d, _ptr(a), _ptr(b), _ptr(c), _ptr(out), n),
+           "mma_oracle_dots")
+    return out
+
+
+class Library:
+    """The same functions bound to another build of the oracle source (used
+    by the tests that plant mistakes in a copy of it)."""
+
+    def __init__(self, path):
+        self.lib = _bind(ctypes.CDLL(path))
+
+    def gemm(self, *a, **k):
+        return gemm(*a, lib=self.lib, **k)
+
+    def gemm_rows(self, *a, **k):
+        return gemm_rows(*a, lib=self.lib, **k)
+
+    def tiles(self, *a, **k):
+        return tiles(*a, lib=self.lib, **k)
+
+    def dots(self, *a, **k):
+        return dots(*a, lib=self.lib, **k)
+
+
+def build_library(src_path, out_path):
+    """Compile an oracle source file (e.g. a modified copy) to out_path."""
+    cmd = ["gcc", "-std=c99", "-D_DEFAULT_SOURCE", "-O1", "-fPIC", "-shared", "-w",
+           "-pthread", "-I", HERE, src_path, "-o", out_path]
+    subprocess.run(cmd, check=True)
+    return Library(out_path)
