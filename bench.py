@@ -1,0 +1,188 @@
+"""Benchmark: bit-exact emulated MACs/s of the 4096^3 FP16 Ampere-model GEMM
+on one MI355X, with its VALU roofline and the CPU oracle timed beside it.
+
+One step = one emulated GEMM D = C + A.B (M = N = K = 4096, A, B FP16
+~ N(0,1), C = +0, Ampere model: 256 chained 16x16x16 steps per output, FP32
+write-back of every step, per-row xorsum fingerprint), inputs resident in
+HBM before the timed region starts.
+
+Prints ONE JSON line.  --gpus above 1 is refused (one GPU per process and
+box; the path shards over rows of D, see the design notes).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+M = N = K = 4096
+MACS = M * N * K
+# Algorithmic integer operations per emulated MAC of the Ampere FP16 model:
+# exact product, exponent add, max, distance, truncating shift, signed add
+# (6 per MAC) plus the per-group normalisation and the per-step FP32
+# write-back amortised over 8 and 16 MACs (about 1 per MAC).
+ALG_OPS_PER_MAC = 7
+# MI355X integer VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one
+# 32-bit integer operation per lane per clock (non-packed).
+VALU_PEAK_OPS = 256 * 64 * 2.4e9
+# The pages' CPU simulator on the same workload: 50.8 s for 4096^3 on an
+# Apple M4 Pro (Hawkeye notes, "Experiments and results", Table 1).
+PAGES_MACS_PER_S = MACS / 50.8
+WORKLOAD = "gemm_4096x4096x4096_fp16_ampere"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU work for the oracle sample")
+    p.add_argument("--cpu-threads", type=int, default=16)
+    return p.parse_args()
+
+
+def traffic_record(kernel_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "gemm_4096_fp16_ampere_hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_source_sha256") != kernel_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_exact_matrix_amd", "csrc")
+    for fn in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, fn), "rb").read())
+    return h.hexdigest()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the GEMM shards over rows of D with no exchange; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_exact_matrix_amd as mm
+    from bit_exact_matrix_amd import inputs as I
+
+    mm.load_library()
+    dev = torch.device("cuda:0")
+    A, B, C = I.gemm_normal(3001, M, N, K)
+    tA = torch.from_numpy(A.view(np.int16)).to(dev)
+    tB = torch.from_numpy(B.view(np.int16)).to(dev)
+    tC = torch.from_numpy(C.view(np.float32)).to(dev)
+    tD = torch.empty((M, N), dtype=torch.float32, device=dev)
+    tX = torch.empty(M, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    # one launch = the whole hot path (with the xorsum epilogue)
+    def one():
+        rc = mm.mma_emulate_gemm_async(0, 0, tA.data_ptr(), tB.data_ptr(), tC.data_ptr(),
+                                       tD.data_ptr(), M, N, K, tX.data_ptr(),
+                                       stream.cuda_stream)
+        if rc:
+            raise mm.MmaEmuError(rc, "mma_emulate_gemm_async")
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+
+    # timed region: K steps bracketed by synchronisation; HIP events on the
+    # launch stream give the per-launch durations
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        one()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ev_total_s = sum(launch_ms) / 1e3
+    ms_per_step = 1e3 * ev_total_s / args.steps
+    value = MACS * args.steps / ev_total_s
+
+    # parity of the timed output against the oracle's full-output digest
+    D = tD.cpu().numpy().view(np.uint32)
+    X = tX.cpu().numpy().view(np.uint32)
+    dig = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))
+    ref = dig.get("gemm_4096_fp16_ampere", {})
+    bit_exact = (hashlib.sha256(D.tobytes()).hexdigest() == ref.get("D_sha256")
+                 and hashlib.sha256(X.tobytes()).hexdigest() == ref.get("xorsum_sha256"))
+
+    avg_launch_s = ev_total_s / args.steps
+    achieved = ALG_OPS_PER_MAC * MACS / avg_launch_s
+    khash = kernel_source_hash()
+    traffic = traffic_record(khash)
+    roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3),
+                "peak": round(VALU_PEAK_OPS / 1e12, 3), "unit": "TOP/s",
+                "frac": round(achieved / VALU_PEAK_OPS, 4), "traffic": traffic,
+                "ops_per_mac": ALG_OPS_PER_MAC,
+                "launch_ms_mean": round(1e3 * avg_launch_s, 4),
+                "launch_ms_min": round(min(launch_ms), 4)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        nth = max(1, min(args.cpu_threads, oracle.num_cpus()))
+        # calibrate on a few rows, then time a sample worth ~cpu_seconds
+        t = time.perf_counter()
+        oracle.gemm_rows("ampere", "fp16", A, B, C, 0, nth, nthreads=nth)
+        per_row = (time.perf_counter() - t) / nth
+        rows = int(max(nth, min(M, args.cpu_seconds / max(per_row, 1e-9))))
+        rows = max(nth, (rows // nth) * nth)
+        t = time.perf_counter()
+        Dr, Xr = oracle.gemm_rows("ampere", "fp16", A, B, C, 0, rows, nthreads=nth)
+        cs = time.perf_counter() - t
+        cpu = {"value": round(rows * N * K / cs, 1), "unit": "MAC/s", "cores": nth,
+               "kind": "oracle", "seconds": round(cs, 2),
+               "sample": f"rows 0..{rows - 1} of D ({rows}x{N}x{K} MACs) of the same GEMM",
+               "sample_matches_gpu": bool(np.array_equal(Dr, D[:rows])
+                                          and np.array_equal(Xr, X[:rows]))}
+
+    out = {
+        "metric": "bit-exact emulated MACs/s, 4096^3 FP16 Ampere model; % of VALU peak",
+        "value": round(value, 1),
+        "unit": "MAC/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(value / PAGES_MACS_PER_S, 1),
+        "dtype": "int32",
+        "data": "synthetic: A, B FP16 ~N(0,1) seed 3001, C = +0",
+        "config": {"workload": WORKLOAD, "M": M, "N": N, "K": K, "model": "ampere",
+                   "input": "fp16", "accumulator": "fp32", "xorsum": "per-row",
+                   "parallelism": "single-gpu"},
+        "bit_exact_vs_oracle": bool(bit_exact),
+        "wall_s_timed": round(wall, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,150 @@
+"""Python binding of libmmaemu.so, the MI355X bit-exact tile-MMA emulator.
+
+Argument marshalling only: every step of the emulation runs in the HIP
+kernels of libmmaemu.so (see include/mmaemu.h for the arithmetic and the
+ABI).  PyTorch supplies device memory and the current stream.  There is no
+CPU fallback: if the library is missing or no GPU is present, the calls
+raise.
+
+The raw C entry points are available under their own names
+(``mma_emulate_gemm``, ``mma_emulate_gemm_async``, ``mma_emulate_tiles``,
+``mma_emulate_strerror``, ``mma_emulate_spec_version``) and take integers
+(device pointers) exactly as the C functions do; ``gemm`` and ``tiles`` wrap
+them for torch tensors.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmmaemu.so")
+
+AMPERE, HOPPER = 0, 1
+FP16, BF16, FP8_E4M3 = 0, 1, 2
+MODELS = {"ampere": AMPERE, "hopper": HOPPER}
+DTYPES = {"fp16": FP16, "bf16": BF16, "e4m3": FP8_E4M3, "fp8_e4m3": FP8_E4M3}
+EXPORTED = ("mma_emulate_gemm", "mma_emulate_gemm_async", "mma_emulate_tiles",
+            "mma_emulate_strerror", "mma_emulate_spec_version")
+
+
+class MmaEmuError(RuntimeError):
+    def __init__(self, code, where):
+        self.code = code
+        super().__init__(f"{where}: {mma_emulate_strerror(code)} (code {code})")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libmmaemu.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it first (__graft_entry__.build())")
+        lib = ctypes.CDLL(path)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.mma_emulate_gemm.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp]
+        lib.mma_emulate_gemm_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp]
+        lib.mma_emulate_tiles.argtypes = [i32, i32, vp, vp, vp, vp, i64, vp, vp]
+        lib.mma_emulate_strerror.argtypes = [i32]
+        lib.mma_emulate_strerror.restype = ctypes.c_char_p
+        lib.mma_emulate_spec_version.argtypes = []
+        for f in (lib.mma_emulate_gemm, lib.mma_emulate_gemm_async, lib.mma_emulate_tiles,
+                  lib.mma_emulate_spec_version):
+            f.restype = i32
+        _lib = lib
+    return _lib
+
+
+# ------------------------------------------------------- raw C entry points
+def mma_emulate_gemm(model, dtype, A, B, C, D, M, N, K, xorsum_out):
+    return load_library().mma_emulate_gemm(model, dtype, A, B, C, D, M, N, K, xorsum_out)
+
+
+def mma_emulate_gemm_async(model, dtype, A, B, C, D, M, N, K, xorsum_out, hip_stream):
+    return load_library().mma_emulate_gemm_async(model, dtype, A, B, C, D, M, N, K,
+                                                 xorsum_out, hip_stream)
+
+
+def mma_emulate_tiles(model, dtype, A, B, C, D, ntiles, xorsum_out, hip_stream):
+    return load_library().mma_emulate_tiles(model, dtype, A, B, C, D, ntiles, xorsum_out,
+                                            hip_stream)
+
+
+def mma_emulate_strerror(code) -> str:
+    return load_library().mma_emulate_strerror(int(code)).decode()
+
+
+def mma_emulate_spec_version() -> int:
+    return load_library().mma_emulate_spec_version()
+
+
+# ------------------------------------------------------------ torch layer
+def _enum(v, table):
+    return table[v.lower()] if isinstance(v, str) else int(v)
+
+
+def _dev_ptr(t, what, nbytes_elem=None):
+    import torch
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{what} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if nbytes_elem is not None and t.element_size() != nbytes_elem:
+        raise TypeError(f"{what}: expected {nbytes_elem}-byte elements, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream_handle(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
+    """Emulated D = C + A.B on the current stream.
+
+    A: M x K and B: K x N device tensors of raw codes (2-byte elements for
+    FP16/BF16, 1-byte for E4M3).  C: optional M x N float32 (bit patterns).
+    Returns (D, xorsum): D float32 M x N, xorsum int32 of M words (bit
+    patterns of the per-row XOR) or None.
+    """
+    import torch
+    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    esz = 1 if d == FP8_E4M3 else 2
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if D is None:
+        D = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    X = torch.empty(M, dtype=torch.int32, device=A.device) if xorsum else None
+    rc = mma_emulate_gemm_async(m, d, _dev_ptr(A, "A", esz), _dev_ptr(B, "B", esz),
+                                _dev_ptr(C, "C", 4), _dev_ptr(D, "D", 4), M, N, K,
+                                _dev_ptr(X, "xorsum"), _stream_handle(stream))
+    if rc != 0:
+        raise MmaEmuError(rc, "mma_emulate_gemm_async")
+    return D, X
+
+
+def tiles(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
+    """ntiles independent 16x16x16 MMAs: A, B [n,16,16] codes, C [n,16,16] f32."""
+    import torch
+    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    esz = 1 if d == FP8_E4M3 else 2
+    n = A.shape[0]
+    if tuple(A.shape) != (n, 16, 16) or tuple(B.shape) != (n, 16, 16):
+        raise ValueError("A and B must be [ntiles, 16, 16]")
+    if D is None:
+        D = torch.empty((n, 16, 16), dtype=torch.float32, device=A.device)
+    X = torch.empty(n, dtype=torch.int32, device=A.device) if xorsum else None
+    rc = mma_emulate_tiles(m, d, _dev_ptr(A, "A", esz), _dev_ptr(B, "B", esz),
+                           _dev_ptr(C, "C", 4), _dev_ptr(D, "D", 4), n,
+                           _dev_ptr(X, "xorsum"), _stream_handle(stream))
+    if rc != 0:
+        raise MmaEmuError(rc, "mma_emulate_tiles")
+    return D, X

@@ -1,0 +1,255 @@
+// mmaemu.hip -- libmmaemu.so: kernels and C ABI of the MI355X bit-exact
+// tile-MMA emulator.  The interface and the arithmetic it implements are
+// documented in include/mmaemu.h.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/mmaemu.h"
+#include "mmaemu_common.h"
+#include "gemm_fast.h"
+
+using namespace mmaemu;
+
+namespace {
+
+constexpr int kSpecVersion = 1;
+
+// ------------------------------------------------------------------ tiles
+// One workgroup per 16x16x16 tile, one lane per output element.
+template <int MODEL, int DT>
+__global__ __launch_bounds__(256) void tiles_kernel(const void* __restrict__ A,
+                                                    const void* __restrict__ B,
+                                                    const uint32_t* C,  // may equal D
+                                                    uint32_t* D,
+                                                    uint32_t* __restrict__ xorsum) {
+  __shared__ uint32_t sa[16][17];
+  __shared__ uint32_t sb[16][17];
+  __shared__ uint32_t wx[4];
+  const int64_t tile = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int i = tid >> 4, j = tid & 15;
+  const int64_t base = tile * 256;
+  sa[i][j] = load_code<DT>(A, base + tid);
+  sb[i][j] = load_code<DT>(B, base + tid);
+  const uint32_t c = C ? C[base + tid] : 0u;
+  __syncthreads();
+  uint32_t a[16], b[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    a[k] = sa[i][k];
+    b[k] = sb[k][j];
+  }
+  const uint32_t d = step_generic<MODEL, DT>(c, a, b);
+  D[base + tid] = d;
+  if (xorsum) {
+    const uint32_t w = wave_xor(d);
+    if ((tid & 63) == 0) wx[tid >> 6] = w;
+    __syncthreads();
+    if (tid == 0) xorsum[tile] = wx[0] ^ wx[1] ^ wx[2] ^ wx[3];
+  }
+}
+
+// --------------------------------------------------- reference GEMM path
+// One lane per output, 256 chained steps read straight from global memory.
+// Kept as the simple, fully general path (any shape, any input bits).
+template <int MODEL, int DT>
+__global__ __launch_bounds__(256) void gemm_reference_kernel(
+    const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C,
+    uint32_t* D, uint32_t* __restrict__ xorsum, int64_t M, int64_t N, int64_t K) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool live = col < N;
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
+    uint32_t c = 0;
+    if (live) {
+      c = C ? C[row * N + col] : 0u;
+      for (int64_t t = 0; t < K / 16; ++t) {
+        uint32_t a[16], b[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          a[k] = load_code<DT>(A, row * K + 16 * t + k);
+          b[k] = load_code<DT>(B, (16 * t + k) * N + col);
+        }
+        c = step_generic<MODEL, DT>(c, a, b);
+      }
+      D[row * N + col] = c;
+    }
+    if (xorsum) {
+      const uint32_t w = wave_xor(live ? c : 0u);
+      if ((threadIdx.x & 63) == 0 && w) atomicXor(&xorsum[row], w);
+    }
+  }
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// ------------------------------------------------------------- plumbing
+thread_local char g_hip_error[256] = "no HIP error recorded";
+
+int hip_fail(hipError_t e, const char* where) {
+  snprintf(g_hip_error, sizeof g_hip_error, "HIP error in %s: %s", where,
+           hipGetErrorString(e));
+  return MMAEMU_ERR_HIP;
+}
+
+int check_model_dtype(int model, int dtype) {
+  if (model != MMAEMU_MODEL_AMPERE && model != MMAEMU_MODEL_HOPPER) return MMAEMU_ERR_MODEL;
+  if (dtype != MMAEMU_DTYPE_FP16 && dtype != MMAEMU_DTYPE_BF16 &&
+      dtype != MMAEMU_DTYPE_FP8_E4M3)
+    return MMAEMU_ERR_DTYPE;
+  if (dtype == MMAEMU_DTYPE_FP8_E4M3 && model != MMAEMU_MODEL_HOPPER)
+    return MMAEMU_ERR_UNSUPPORTED;
+  return MMAEMU_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+bool overlap(Range a, Range b) {
+  return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+Range range_of(const void* p, int64_t bytes) {
+  const uintptr_t lo = (uintptr_t)p;
+  return Range{lo, p ? lo + (uintptr_t)bytes : lo};
+}
+
+// A, B, C read-only; D and xorsum written.  D == C exactly is allowed.
+int check_alias(const void* A, int64_t abytes, const void* B, int64_t bbytes,
+                const void* C, const void* D, int64_t cdbytes, const void* X,
+                int64_t xbytes) {
+  const Range ra = range_of(A, abytes), rb = range_of(B, bbytes);
+  const Range rc = range_of(C, cdbytes), rd = range_of(D, cdbytes);
+  const Range rx = range_of(X, xbytes);
+  if (overlap(rd, ra) || overlap(rd, rb) || overlap(rx, ra) || overlap(rx, rb) ||
+      overlap(rx, rc) || overlap(rx, rd))
+    return MMAEMU_ERR_ALIAS;
+  if (C && C != D && overlap(rc, rd)) return MMAEMU_ERR_ALIAS;
+  return MMAEMU_OK;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a == 0 || b == 0) {
+    *out = 0;
+    return true;
+  }
+  if (a > INT64_MAX / b) return false;
+  *out = a * b;
+  return true;
+}
+
+template <int MODEL, int DT>
+hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, uint32_t* D,
+                       uint32_t* X, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  if (X) {
+    const int64_t blocks = (M + 255) / 256;
+    fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(X, M);
+  }
+  if (gemm_fast_supported(M, N, K)) {
+    gemm_fast_launch<MODEL, DT>(A, B, C, D, X, M, N, K, s);
+  } else {
+    const int64_t cb = (N + 255) / 256;
+    const int64_t rows = M < 32768 ? M : 32768;
+    gemm_reference_kernel<MODEL, DT>
+        <<<dim3((unsigned)cb, (unsigned)rows), dim3(256), 0, s>>>(A, B, C, D, X, M, N, K);
+  }
+  return hipGetLastError();
+}
+
+template <int MODEL, int DT>
+hipError_t launch_tiles(const void* A, const void* B, const uint32_t* C, uint32_t* D,
+                        uint32_t* X, int64_t ntiles, hipStream_t s) {
+  tiles_kernel<MODEL, DT><<<dim3((unsigned)ntiles), dim3(256), 0, s>>>(A, B, C, D, X);
+  return hipGetLastError();
+}
+
+#define MMAEMU_DISPATCH(model, dtype, FN, ...)                                  \
+  ((model) == MMAEMU_MODEL_AMPERE                                               \
+       ? ((dtype) == MMAEMU_DTYPE_FP16 ? FN<kAmpere, kFP16>(__VA_ARGS__)        \
+                                       : FN<kAmpere, kBF16>(__VA_ARGS__))       \
+       : ((dtype) == MMAEMU_DTYPE_FP16                                          \
+              ? FN<kHopper, kFP16>(__VA_ARGS__)                                 \
+              : ((dtype) == MMAEMU_DTYPE_BF16 ? FN<kHopper, kBF16>(__VA_ARGS__) \
+                                              : FN<kHopper, kE4M3>(__VA_ARGS__))))
+
+int gemm_impl(int model, int dtype, const void* A, const void* B, const float* C,
+              float* D, int64_t M, int64_t N, int64_t K, uint32_t* xorsum,
+              hipStream_t s) {
+  int rc = check_model_dtype(model, dtype);
+  if (rc) return rc;
+  if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return MMAEMU_ERR_SHAPE;
+  const int64_t esz = dtype == MMAEMU_DTYPE_FP8_E4M3 ? 1 : 2;
+  int64_t mk, kn, mn, ab, bb, cb;
+  if (!mul_ok(M, K, &mk) || !mul_ok(K, N, &kn) || !mul_ok(M, N, &mn) ||
+      !mul_ok(mk, esz, &ab) || !mul_ok(kn, esz, &bb) || !mul_ok(mn, 4, &cb))
+    return MMAEMU_ERR_SHAPE;
+  if (N > (int64_t)INT32_MAX || M > (int64_t)INT32_MAX * 256) return MMAEMU_ERR_SHAPE;
+  if (mn == 0) return MMAEMU_OK;
+  if (!D || (K > 0 && (!A || !B))) return MMAEMU_ERR_NULL;
+  rc = check_alias(A, K ? ab : 0, B, K ? bb : 0, C, D, cb, xorsum, xorsum ? M * 4 : 0);
+  if (rc) return rc;
+  const hipError_t e = MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C,
+                                       (uint32_t*)D, xorsum, M, N, K, s);
+  if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm launch");
+  return MMAEMU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mma_emulate_gemm_async(int model, int dtype, const void* A, const void* B,
+                           const float* C, float* D, int64_t M, int64_t N, int64_t K,
+                           uint32_t* xorsum_out, void* hip_stream) {
+  return gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, (hipStream_t)hip_stream);
+}
+
+int mma_emulate_gemm(int model, int dtype, const void* A, const void* B, const float* C,
+                     float* D, int64_t M, int64_t N, int64_t K, uint32_t* xorsum_out) {
+  const int rc = gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, nullptr);
+  if (rc) return rc;
+  const hipError_t e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm synchronize");
+  return MMAEMU_OK;
+}
+
+int mma_emulate_tiles(int model, int dtype, const void* A, const void* B, const float* C,
+                      float* D, int64_t ntiles, uint32_t* xorsum_out, void* hip_stream) {
+  int rc = check_model_dtype(model, dtype);
+  if (rc) return rc;
+  if (ntiles < 0 || ntiles > (int64_t)INT32_MAX) return MMAEMU_ERR_SHAPE;
+  if (ntiles == 0) return MMAEMU_OK;
+  if (!A || !B || !D) return MMAEMU_ERR_NULL;
+  const int64_t esz = dtype == MMAEMU_DTYPE_FP8_E4M3 ? 1 : 2;
+  rc = check_alias(A, ntiles * 256 * esz, B, ntiles * 256 * esz, C, D, ntiles * 1024,
+                   xorsum_out, xorsum_out ? ntiles * 4 : 0);
+  if (rc) return rc;
+  const hipError_t e =
+      MMAEMU_DISPATCH(model, dtype, launch_tiles, A, B, (const uint32_t*)C, (uint32_t*)D,
+                      xorsum_out, ntiles, (hipStream_t)hip_stream);
+  if (e != hipSuccess) return hip_fail(e, "mma_emulate_tiles launch");
+  return MMAEMU_OK;
+}
+
+const char* mma_emulate_strerror(int code) {
+  switch (code) {
+    case MMAEMU_OK: return "ok";
+    case MMAEMU_ERR_MODEL: return "unknown model";
+    case MMAEMU_ERR_DTYPE: return "unknown dtype";
+    case MMAEMU_ERR_UNSUPPORTED: return "FP8 E4M3 exists only with the Hopper model";
+    case MMAEMU_ERR_SHAPE: return "bad shape (negative, K not a multiple of 16, or too large)";
+    case MMAEMU_ERR_NULL: return "a required pointer is NULL";
+    case MMAEMU_ERR_ALIAS: return "buffers overlap (only D == C is allowed)";
+    case MMAEMU_ERR_HIP: return g_hip_error;
+    default: return "unknown error code";
+  }
+}
+
+int mma_emulate_spec_version(void) { return kSpecVersion; }
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+/*
+ * mmaemu.h -- C ABI of the MI355X bit-exact tile-MMA emulator (libmmaemu.so).
+ *
+ * WHAT IT COMPUTES
+ *   D = C + A*B, built from chained 16x16x16 matrix-multiply-accumulate
+ *   steps, each rounded the way the Hawkeye study recovered for NVIDIA
+ *   tensor cores ("Hawkeye: Reproducing GPU-Level Non-Determinism
+ *   (MLSys 2026)", reading notes: "Key observations" 1-4, "Core method /
+ *   Target Tests" table, "Recovered Ampere FP16 pipeline", "Experiments and
+ *   results").  For one output (i, j) of one step t with C the running FP32
+ *   value and P1..P16 the products A[i][16t+k-1]*B[16t+k-1][j]:
+ *     - products are exact and unnormalised: sign sa^sb, exponent Ea+Eb,
+ *       integer significand ma*mb; subnormal inputs keep exponent emin and
+ *       are not renormalised (observations 1 and 3);
+ *     - a group sum takes the largest exponent among its non-zero terms,
+ *       puts every term on the grid 2^(emax-F) by truncating its magnitude
+ *       (round toward zero, observation 3) and adds the integers exactly;
+ *     - AMPERE: S1 = C + P1..P8 with F = 23, cut to 24 significant bits
+ *       (toward zero, exponent unbounded), then V = S1 + P9..P16 with F = 23
+ *       (the two-stage pyramid of observation 2);
+ *       HOPPER: V = C + P1..P16 in one group with F = 24 (25-bit width);
+ *     - V is written back to FP32 toward zero with gradual underflow;
+ *       |V| >= 2^128 becomes +-inf (the BF16 overflow rule of "Experiments
+ *       and results", applied to every dtype);
+ *     - specials: any NaN, inf*0, or +inf with -inf gives NaN 0x7FC00000,
+ *       otherwise an infinite term gives that infinity; a group of only
+ *       zero terms gives -0 iff all of them are -0, an exact cancellation
+ *       gives +0, an FP32 underflow keeps V's sign;
+ *     - the result is the next step's C; after K/16 steps it is D
+ *       (observation 4: a MatMul is a deterministic sequence of tiles).
+ *   FP8 E4M3 (OCP "FN": no inf, NaN = S.1111.111) exists only with HOPPER.
+ *   The optional fingerprint is the XOR of the uint32 patterns of each row
+ *   of D ("How AEGIS Turns Training Redundancy into Evidence", section
+ *   "Redundancy already exists in the training computation").
+ *
+ * MEMORY AND LAYOUT
+ *   Every pointer is a DEVICE pointer on the current HIP device, owned by
+ *   the caller; the library keeps nothing between calls and allocates no
+ *   device memory.
+ *   A  M x K row-major raw codes: uint16 (FP16, BF16) or uint8 (E4M3)
+ *   B  K x N row-major raw codes, same type
+ *   C  M x N row-major FP32 (read as bit patterns); NULL means all +0.0
+ *   D  M x N row-major FP32 bit patterns; D == C (exactly) is allowed
+ *   xorsum_out  NULL, or M uint32 words (overwritten, not accumulated)
+ *   Shapes: M >= 0, N >= 0, K >= 0 with K a multiple of 16.  Empty
+ *   operands are allowed (K = 0 gives D = C).
+ *
+ * ERRORS
+ *   Argument errors are reported before anything is enqueued and leave all
+ *   buffers untouched.  A failed launch returns MMAEMU_ERR_HIP; the text of
+ *   the HIP error is available from mma_emulate_strerror(MMAEMU_ERR_HIP)
+ *   on the same thread.  No C++ exception crosses this interface.
+ *
+ * DETERMINISM
+ *   The same inputs give the same D and xorsum bits on every call, stream
+ *   and device.  Each D element is written by exactly one lane; there is no
+ *   split-K and no atomic accumulation of D.
+ */
+#ifndef MMAEMU_H
+#define MMAEMU_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* arithmetic models: the architectures the Hawkeye study characterised */
+enum { MMAEMU_MODEL_AMPERE = 0, MMAEMU_MODEL_HOPPER = 1 };
+
+/* input formats: FP16, BF16 and FP8 E4M3 ("One-sentence summary") */
+enum { MMAEMU_DTYPE_FP16 = 0, MMAEMU_DTYPE_BF16 = 1, MMAEMU_DTYPE_FP8_E4M3 = 2 };
+
+enum {
+  MMAEMU_OK = 0,
+  MMAEMU_ERR_MODEL = -1,       /* unknown model */
+  MMAEMU_ERR_DTYPE = -2,       /* unknown dtype */
+  MMAEMU_ERR_UNSUPPORTED = -3, /* E4M3 with the Ampere model */
+  MMAEMU_ERR_SHAPE = -4,       /* negative size, K not a multiple of 16, overflow */
+  MMAEMU_ERR_NULL = -5,        /* a required pointer is NULL */
+  MMAEMU_ERR_ALIAS = -6,       /* buffers overlap other than D == C */
+  MMAEMU_ERR_HIP = -7          /* a HIP launch or runtime call failed */
+};
+
+/* Emulated GEMM, blocking: enqueued on the null stream of the current
+ * device, which is then synchronised.  Arguments as described above. */
+int mma_emulate_gemm(int model, int dtype, const void *A, const void *B,
+                     const float *C, float *D, int64_t M, int64_t N, int64_t K,
+                     uint32_t *xorsum_out);
+
+/* Same contract, enqueued on hip_stream (a hipStream_t; NULL = null
+ * stream); returns after enqueue.  The buffers must stay valid until the
+ * stream has run the work. */
+int mma_emulate_gemm_async(int model, int dtype, const void *A, const void *B,
+                           const float *C, float *D, int64_t M, int64_t N,
+                           int64_t K, uint32_t *xorsum_out, void *hip_stream);
+
+/* ntiles independent 16x16x16 MMA steps (the unit the Hawkeye study audits,
+ * "Key observation 1"): A, B are [ntiles][16][16] row-major codes, C, D are
+ * [ntiles][16][16] FP32 (C may be NULL, D may equal C); xorsum_out is NULL
+ * or ntiles words, each the XOR of its tile's 256 D words.  Enqueued on
+ * hip_stream; returns after enqueue. */
+int mma_emulate_tiles(int model, int dtype, const void *A, const void *B,
+                      const float *C, float *D, int64_t ntiles,
+                      uint32_t *xorsum_out, void *hip_stream);
+
+/* Text for a return code (thread-local for MMAEMU_ERR_HIP: names the last
+ * HIP error seen on this thread).  Never NULL. */
+const char *mma_emulate_strerror(int code);
+
+/* Revision of the arithmetic rules above; bumped whenever a rule changes. */
+int mma_emulate_spec_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

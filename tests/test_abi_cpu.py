@@ -1,0 +1,83 @@
+"""Host-side checks of libmmaemu.so that need no GPU: the library loads,
+exports every entry point include/mmaemu.h declares, and rejects bad
+arguments before anything is enqueued (no compute call is made here)."""
+import os
+import re
+
+import pytest
+
+import bit_exact_matrix_amd as mm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(mma_\w+)\s*\(", text, re.M))
+    return names
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = mm.load_library()
+    declared = _declared()
+    assert declared >= set(mm.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_strerror_and_version():
+    assert mm.mma_emulate_spec_version() >= 1
+    for code in range(-7, 1):
+        assert isinstance(mm.mma_emulate_strerror(code), str)
+    assert "unknown" in mm.mma_emulate_strerror(42)
+
+
+# Fake, never-dereferenced device addresses: every call below must fail
+# argument validation before any HIP call.
+A, B, C, D, X = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 0, A, B, C, D, 32, 32, 32, X), -1),           # unknown model
+    ((0, 9, A, B, C, D, 32, 32, 32, X), -2),           # unknown dtype
+    ((0, 2, A, B, C, D, 32, 32, 32, X), -3),           # E4M3 with Ampere
+    ((0, 0, A, B, C, D, 32, 32, 24, X), -4),           # K not a multiple of 16
+    ((0, 0, A, B, C, D, -1, 32, 32, X), -4),           # negative M
+    ((0, 0, A, B, C, D, 1 << 40, 1 << 40, 32, X), -4),  # size overflow
+    ((0, 0, A, B, C, 0, 32, 32, 32, X), -5),           # NULL D
+    ((0, 0, 0, B, C, D, 32, 32, 32, X), -5),           # NULL A with K > 0
+    ((0, 0, A, B, C, A + 64, 32, 32, 32, X), -6),      # D overlaps A
+    ((0, 0, A, B, C, C + 4, 32, 32, 32, X), -6),       # D partially overlaps C
+    ((0, 0, A, B, C, D, 32, 32, 32, D + 8), -6),       # xorsum inside D
+])
+def test_gemm_argument_errors(args, code):
+    assert mm.mma_emulate_gemm_async(*args, None) == code
+
+
+def test_gemm_empty_is_a_no_op():
+    # M = 0 or N = 0: nothing to compute, nothing enqueued
+    assert mm.mma_emulate_gemm_async(0, 0, A, B, C, D, 0, 32, 32, X, None) == 0
+    assert mm.mma_emulate_gemm_async(1, 2, A, B, C, D, 32, 0, 32, X, None) == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((3, 0, A, B, C, D, 4, X), -1),
+    ((0, 2, A, B, C, D, 4, X), -3),
+    ((0, 0, A, B, C, D, -4, X), -4),
+    ((0, 0, A, B, C, 0, 4, X), -5),
+    ((0, 0, A, B, C, B, 4, X), -6),
+])
+def test_tiles_argument_errors(args, code):
+    assert mm.mma_emulate_tiles(*args, None) == code
+
+
+def test_tiles_empty_is_a_no_op():
+    assert mm.mma_emulate_tiles(0, 0, A, B, C, D, 0, X, None) == 0
+
+
+def test_in_place_c_equals_d_passes_validation_only():
+    # D == C is allowed; with M = 0 nothing runs, so this checks the alias rule alone
+    assert mm.mma_emulate_gemm_async(0, 0, A, B, C, C, 0, 16, 16, X, None) == 0
