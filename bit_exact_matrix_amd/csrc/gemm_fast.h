@@ -1,11 +1,480 @@
-// gemm_fast.h -- tiled GEMM path (placeholder until the LDS-tiled kernel lands).
+// gemm_fast.h -- LDS-tiled integer-VALU GEMM of the emulated tile MMA.
+//
+// Same arithmetic as step_generic (mmaemu_common.h; rules in
+// include/mmaemu.h), reorganised for gfx950:
+//
+//  * a 256-lane workgroup owns a 64x64 block of D; each lane owns a 4x4
+//    register tile and walks the K/16 chained MMA steps, carrying its 16
+//    accumulators in registers in a decoded form (no FP32 pack/unpack per
+//    step);
+//  * per step the workgroup loads the 64x16 A slice and 16x64 B slice once
+//    (raw codes, coalesced) and unpacks them into LDS (double-buffered):
+//    A: significand pre-shifted onto the group grid, sign mask, exponent;
+//    B: signed significand, sign mask, exponent; plus per-row / per-column
+//    sign bitmasks for the group;
+//  * exponents live as 16-bit "negated biased" values NE = bias - E, two per
+//    register, so one packed add gives the exponents of two products and one
+//    packed min their running maximum (pass 1); a saturating packed add of
+//    NE - min + 0xFFE0 then yields both alignment distances already clamped
+//    to 31 in their low 5 bits (the shifter only reads 5 bits);
+//  * pass 2 per product: v_mad_i32_i24 forms the exact product in one's
+//    complement of B's sign (b*a + sb = m ^ sb), an arithmetic shift by the
+//    clamped distance truncates the MAGNITUDE toward zero
+//    (asr(m ^ s, d) = (m >> d) ^ s), and v_xad_u32 applies A's sign and
+//    accumulates; the +1 owed by every negative term is added once per
+//    group as a popcount of the XOR of the two sign bitmasks;
+//  * every rare case -- a zero group sum, an FP32-subnormal result, an inf
+//    or NaN operand -- is detected with a range check and recomputed for
+//    that output alone by step_generic from the raw codes kept in LDS.
 #pragma once
-#include <hip/hip_runtime.h>
-#include <stdint.h>
+
+#include "mmaemu_common.h"
 
 namespace mmaemu {
-inline bool gemm_fast_supported(int64_t, int64_t, int64_t) { return false; }
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+namespace fastk {
+
+constexpr int BM = 64, BN = 64, NT = 256;
+// 16-bit exponent codes.  Operand: NE = 0x2000 - E; zero operand 0x3000
+// (E = -4096, below every real term); inf/NaN operand 0x0400 (E = 7168,
+// above every real term so the result lands out of range).
+constexpr uint32_t OP_BIAS = 0x2000, OP_ZERO = 0x3000, OP_SPECIAL = 0x0400;
+// Terms (products, C, the Ampere stage-1 sum): NE = 0x4000 - E.
+constexpr int T_BIAS = 0x4000;
+constexpr uint32_t C_ZERO = 0x6000;  // E = -8192
+constexpr uint32_t C_NAN = 0x2000;   // E = 8192: always recomputed
+constexpr uint32_t C_INF = 0x3C00;   // E = 1024: dominates every product
+// A fast-path result must have its leading-bit exponent in [-126, 2047];
+// [128, 2047] is an FP32 overflow and becomes the inf state.
+constexpr uint32_t NE_OK_LO = T_BIAS - 2047, NE_OK_SPAN = 2047 + 126;
+constexpr uint32_t NE_OVF = T_BIAS - 128;
+constexpr unsigned short SAT = 0xFFE0;
+
+struct Stage {
+  uint32_t a_val[16][BM];  // A significand << (F - 2t)
+  int32_t a_sgn[16][BM];   // 0 / -1
+  uint32_t a_ne[8][BM];    // NE of k = 2p | NE of k = 2p+1 << 16
+  uint32_t a_msk[2][BM];   // sign bits of the row's group products
+  int32_t b_val[16][BN];   // signed B significand
+  int32_t b_sgn[16][BN];
+  uint32_t b_ne[8][BN];
+  uint32_t b_msk[2][BN];
+  uint16_t a_raw[BM][16];  // raw codes for the per-output recompute
+  uint16_t b_raw[16][BN];
+};
+
+__device__ __forceinline__ u16x2 as2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
+__device__ __forceinline__ uint32_t as32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ u16x2 splat_lo(uint32_t x) {
+  return u16x2{(unsigned short)x, (unsigned short)x};
+}
+// (a ^ b) + c in one VALU op (the compiler prefers xor + add3 pairs).
+__device__ __forceinline__ int xad(int a, int b, int c) {
+  int r;
+  asm("v_xad_u32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+// One operand: significand, sign mask, 16-bit exponent code.
+template <int DT>
+__device__ __forceinline__ void unpack(uint32_t code, uint32_t& m, int& s, uint32_t& ne) {
+  using F = Fmt<DT>;
+  constexpr uint32_t fmask = (1u << F::t) - 1u;
+  constexpr uint32_t emask = (1u << F::eb) - 1u;
+  const uint32_t frac = code & fmask;
+  const uint32_t ef = (code >> F::t) & emask;
+  s = -(int)((code >> (F::t + F::eb)) & 1u);
+  const bool special = F::has_inf ? (ef == emask) : (ef == emask && frac == fmask);
+  const bool sub = ef == 0;
+  m = sub ? frac : (frac | (1u << F::t));
+  const int E = sub ? 1 - F::bias : (int)ef - F::bias;
+  ne = special ? OP_SPECIAL : (m == 0 ? OP_ZERO : (uint32_t)((int)OP_BIAS - E));
+  if (special) m = 0;
+}
+
+// Accumulator state <-> FP32 bits.  X = M ^ s with M the significand on
+// the group grid (24 bits, << (F-23)); NE = 0x4000 - E in the low half.
 template <int MODEL, int DT>
-inline void gemm_fast_launch(const void*, const void*, const uint32_t*, uint32_t*, uint32_t*,
-                             int64_t, int64_t, int64_t, hipStream_t) {}
+__device__ __forceinline__ void bits_to_state(uint32_t bits, int& X, uint32_t& NE) {
+  constexpr int F = Model<MODEL>::F;
+  const int s = (int)bits >> 31;
+  const uint32_t ef = (bits >> 23) & 0xFFu, fr = bits & 0x7FFFFFu;
+  uint32_t m, ne;
+  if (ef == 0xFFu) {
+    m = 0x800000u;
+    ne = fr ? C_NAN : C_INF;
+  } else if (ef == 0) {
+    m = fr;  // subnormal: exponent -126, not renormalised
+    ne = fr ? (uint32_t)(T_BIAS + 126) : C_ZERO;
+  } else {
+    m = fr | 0x800000u;
+    ne = (uint32_t)(T_BIAS - ((int)ef - 127));
+  }
+  X = (int)(m << (F - 23)) ^ s;
+  NE = ne;
+}
+
+template <int MODEL>
+__device__ __forceinline__ uint32_t state_to_bits(int X, uint32_t NE) {
+  constexpr int F = Model<MODEL>::F;
+  const int s = X >> 31;
+  const uint32_t sign = (uint32_t)s & 0x80000000u;
+  const uint32_t m = (uint32_t)(X ^ s) >> (F - 23);
+  const uint32_t ne = NE & 0xFFFFu;
+  if (ne == C_NAN) return kNaN;
+  if (ne == C_ZERO) return sign;
+  const int E = T_BIAS - (int)ne;
+  if (E >= 128) return sign | kPosInf;
+  if (m < 0x800000u) return sign | m;  // FP32 subnormal (E = -126)
+  return sign | ((uint32_t)(E + 127) << 23) | (m & 0x7FFFFFu);
+}
+
+// Recompute one output's step from raw codes (rare path).
+template <int MODEL, int DT>
+__device__ __noinline__ uint2 slow_step(const Stage* st, int row, int col, int Xold,
+                                        uint32_t NEold) {
+  uint32_t a[16], b[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    a[k] = st->a_raw[row][k];
+    b[k] = st->b_raw[k][col];
+  }
+  const uint32_t c = state_to_bits<MODEL>(Xold, NEold);
+  const uint32_t r = step_generic<MODEL, DT>(c, a, b);
+  int X;
+  uint32_t NE;
+  bits_to_state<MODEL, DT>(r, X, NE);
+  return make_uint2((uint32_t)X, NE);
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t ld_code(const void* p, int64_t idx) {
+  return load_code<DT>(p, idx);
+}
+
+// Unpack this lane's share of the next step into stage st: lane
+// (k = t & 15, q = t >> 4) handles A rows 4q..4q+3 and B cols 4q..4q+3 at k.
+template <int MODEL, int DT>
+__device__ __forceinline__ void produce(Stage* st, const uint32_t (&ca)[4],
+                                        const uint32_t (&cb)[4], int t) {
+  constexpr int F = Model<MODEL>::F;
+  constexpr int pshift = F - 2 * Fmt<DT>::t;
+  const int k = t & 15, q = t >> 4;
+  uint32_t av[4], ane[4], bne[4];
+  int as[4], bv[4], bs[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    uint32_t m, ne;
+    int s;
+    unpack<DT>(ca[u], m, s, ne);
+    av[u] = m << pshift;
+    as[u] = s;
+    ane[u] = ne;
+    unpack<DT>(cb[u], m, s, ne);
+    bv[u] = s ? -(int)m : (int)m;
+    bs[u] = s;
+    bne[u] = ne;
+  }
+  *(uint4*)&st->a_val[k][4 * q] = make_uint4(av[0], av[1], av[2], av[3]);
+  *(int4*)&st->a_sgn[k][4 * q] = make_int4(as[0], as[1], as[2], as[3]);
+  *(int4*)&st->b_val[k][4 * q] = make_int4(bv[0], bv[1], bv[2], bv[3]);
+  *(int4*)&st->b_sgn[k][4 * q] = make_int4(bs[0], bs[1], bs[2], bs[3]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    st->a_raw[4 * q + u][k] = (uint16_t)ca[u];
+    st->b_raw[k][4 * q + u] = (uint16_t)cb[u];
+  }
+  // exponent pairs (k even, k odd): the partner is the adjacent lane
+  uint32_t pa[4], pb[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    pa[u] = __shfl_xor(ane[u], 1, 64);
+    pb[u] = __shfl_xor(bne[u], 1, 64);
+  }
+  if ((k & 1) == 0) {
+    *(uint4*)&st->a_ne[k >> 1][4 * q] =
+        make_uint4(ane[0] | pa[0] << 16, ane[1] | pa[1] << 16, ane[2] | pa[2] << 16,
+                   ane[3] | pa[3] << 16);
+    *(uint4*)&st->b_ne[k >> 1][4 * q] =
+        make_uint4(bne[0] | pb[0] << 16, bne[1] | pb[1] << 16, bne[2] | pb[2] << 16,
+                   bne[3] | pb[3] << 16);
+  }
+  // sign bitmasks: a ballot over the wave gives, for each 16-lane group,
+  // the 16 sign bits (k = 0..15) of one row / column
+  const int g = (t & 63) >> 4;
+  uint32_t am[4], bm[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const uint64_t ba = __ballot(as[u] != 0);
+    const uint64_t bb = __ballot(bs[u] != 0);
+    am[u] = (uint32_t)(ba >> (16 * g)) & 0xFFFFu;
+    bm[u] = (uint32_t)(bb >> (16 * g)) & 0xFFFFu;
+  }
+  if (k == 0) {
+    if (MODEL == kAmpere) {
+      *(uint4*)&st->a_msk[0][4 * q] = make_uint4(am[0] & 0xFF, am[1] & 0xFF, am[2] & 0xFF, am[3] & 0xFF);
+      *(uint4*)&st->a_msk[1][4 * q] = make_uint4(am[0] >> 8, am[1] >> 8, am[2] >> 8, am[3] >> 8);
+      *(uint4*)&st->b_msk[0][4 * q] = make_uint4(bm[0] & 0xFF, bm[1] & 0xFF, bm[2] & 0xFF, bm[3] & 0xFF);
+      *(uint4*)&st->b_msk[1][4 * q] = make_uint4(bm[0] >> 8, bm[1] >> 8, bm[2] >> 8, bm[3] >> 8);
+    } else {
+      *(uint4*)&st->a_msk[0][4 * q] = make_uint4(am[0], am[1], am[2], am[3]);
+      *(uint4*)&st->b_msk[0][4 * q] = make_uint4(bm[0], bm[1], bm[2], bm[3]);
+    }
+  }
+}
+
+// Global loads of step s for lane t (zero codes outside the matrix).
+template <int DT>
+__device__ __forceinline__ void fetch(const void* A, const void* B, int64_t M, int64_t N,
+                                      int64_t K, int64_t bm, int64_t bn, int64_t s, int t,
+                                      uint32_t (&ca)[4], uint32_t (&cb)[4]) {
+  const int k = t & 15, q = t >> 4;
+  const int64_t kk = 16 * s + k;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t row = bm + 4 * q + u;
+    ca[u] = row < M ? ld_code<DT>(A, row * K + kk) : 0u;
+    const int64_t col = bn + 4 * q + u;
+    cb[u] = col < N ? ld_code<DT>(B, kk * N + col) : 0u;
+  }
+}
+
+// One group of products for the lane's 4x4 outputs.
+//   p0, np: first pair and pair count of the group.
+//   ne_t / X_t: the group's extra term (C, or the Ampere stage-1 sum).
+// Returns S (signed exact group sum on the grid of the group's emax) and
+// mn (= 0x4000 - emax, both halves).
+template <int NP, bool STORE_ES>
+__device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, int gmask,
+                                      const uint32_t (&ne_t)[4][4], const int (&X_t)[4][4],
+                                      int (&S)[4][4], uint32_t (&mn_out)[4][4]) {
+  u16x2 mn[4][4];
+  u16x2 es[STORE_ES ? NP : 1][4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mn[r][c] = splat_lo(ne_t[r][c]);
+  // pass 1: exponents of every product and their running maximum
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint4 a4 = *(const uint4*)&st->a_ne[p0 + p][4 * ty];
+    const uint4 b4 = *(const uint4*)&st->b_ne[p0 + p][4 * tx];
+    const uint32_t a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const u16x2 e = as2(a[r]) + as2(b[c]);
+        if constexpr (STORE_ES) es[p][r][c] = e;
+        mn[r][c] = __builtin_elementwise_min(mn[r][c], e);
+      }
+  }
+  u16x2 K[4][4];
+  int acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      mn[r][c] = __builtin_elementwise_min(mn[r][c], mn[r][c].yx);
+      K[r][c] = u16x2{SAT, SAT} - mn[r][c];
+      // the extra term: one's complement significand, +1 if negative
+      const u16x2 w = __builtin_elementwise_add_sat(splat_lo(ne_t[r][c]), K[r][c]);
+      const int X = X_t[r][c];
+      acc[r][c] = (X >> (as32(w) & 31)) - (X >> 31);
+    }
+  // pass 2: products, truncating alignment, signed accumulation
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const int k0 = 2 * (p0 + p), k1 = k0 + 1;
+    const uint4 av0 = *(const uint4*)&st->a_val[k0][4 * ty];
+    const uint4 av1 = *(const uint4*)&st->a_val[k1][4 * ty];
+    const int4 as0 = *(const int4*)&st->a_sgn[k0][4 * ty];
+    const int4 as1 = *(const int4*)&st->a_sgn[k1][4 * ty];
+    const int4 bv0 = *(const int4*)&st->b_val[k0][4 * tx];
+    const int4 bv1 = *(const int4*)&st->b_val[k1][4 * tx];
+    const int4 bs0 = *(const int4*)&st->b_sgn[k0][4 * tx];
+    const int4 bs1 = *(const int4*)&st->b_sgn[k1][4 * tx];
+    const uint32_t a0[4] = {av0.x, av0.y, av0.z, av0.w}, a1[4] = {av1.x, av1.y, av1.z, av1.w};
+    const int sa0[4] = {as0.x, as0.y, as0.z, as0.w}, sa1[4] = {as1.x, as1.y, as1.z, as1.w};
+    const int b0[4] = {bv0.x, bv0.y, bv0.z, bv0.w}, b1[4] = {bv1.x, bv1.y, bv1.z, bv1.w};
+    const int sb0[4] = {bs0.x, bs0.y, bs0.z, bs0.w}, sb1[4] = {bs1.x, bs1.y, bs1.z, bs1.w};
+    uint32_t ane[4] = {0, 0, 0, 0}, bne[4] = {0, 0, 0, 0};
+    if constexpr (!STORE_ES) {
+      const uint4 a4 = *(const uint4*)&st->a_ne[p0 + p][4 * ty];
+      const uint4 b4 = *(const uint4*)&st->b_ne[p0 + p][4 * tx];
+      ane[0] = a4.x, ane[1] = a4.y, ane[2] = a4.z, ane[3] = a4.w;
+      bne[0] = b4.x, bne[1] = b4.y, bne[2] = b4.z, bne[3] = b4.w;
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u16x2 e;
+        if constexpr (STORE_ES) {
+          e = es[p][r][c];
+        } else {
+          e = as2(ane[r]) + as2(bne[c]);
+        }
+        const uint32_t w = as32(__builtin_elementwise_add_sat(e, K[r][c]));
+        const int x0 = __mul24(b0[c], (int)a0[r]) + sb0[c];
+        const int x1 = __mul24(b1[c], (int)a1[r]) + sb1[c];
+        const int t0 = x0 >> (w & 31);
+        const int t1 = x1 >> ((w >> 16) & 31);
+        acc[r][c] = xad(t0, sa0[r], acc[r][c]);
+        acc[r][c] = xad(t1, sa1[r], acc[r][c]);
+      }
+  }
+  // +1 for every negative product: popcount of the XOR of the sign masks
+  const uint4 am = *(const uint4*)&st->a_msk[gmask][4 * ty];
+  const uint4 bmk = *(const uint4*)&st->b_msk[gmask][4 * tx];
+  const uint32_t ma[4] = {am.x, am.y, am.z, am.w}, mb[4] = {bmk.x, bmk.y, bmk.z, bmk.w};
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      S[r][c] = acc[r][c] + __popc(ma[r] ^ mb[c]);
+      mn_out[r][c] = as32(mn[r][c]);
+    }
+}
+
+// Normalise a group sum: one's complement 24-bit significand (shifted by
+// extra bits onto the next group's grid) and its exponent code.
+template <int EXTRA, int F>
+__device__ __forceinline__ void normalise(int S, uint32_t mn, int& X, uint32_t& NE) {
+  const int s = S >> 31;
+  const uint32_t mag = (uint32_t)((S ^ s) - s);
+  const uint32_t lz = __clz(mag);
+  const uint32_t m = ((mag << lz) >> 8) << EXTRA;
+  X = (int)m ^ s;
+  // leading-bit exponent L = emax - F + 31 - lz  ->  NE = mn + F - 31 + lz
+  NE = (mn & 0xFFFFu) + (uint32_t)(F - 31) + lz;
+}
+
+template <int MODEL, int DT>
+__global__ __launch_bounds__(NT, 2) void gemm_fast_kernel(
+    const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, uint32_t* D,
+    uint32_t* __restrict__ xorsum, int64_t M, int64_t N, int64_t K) {
+  constexpr int F = Model<MODEL>::F;
+  __shared__ Stage stage[2];
+  const int t = threadIdx.x;
+  const int ty = t >> 4, tx = t & 15;
+  const int64_t bm = (int64_t)blockIdx.y * BM, bn = (int64_t)blockIdx.x * BN;
+  const int64_t nsteps = K / 16;
+
+  int X[4][4];
+  uint32_t NE[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t row = bm + 4 * ty + r, col = bn + 4 * tx + c;
+      const uint32_t cbits = (C && row < M && col < N) ? C[row * N + col] : 0u;
+      bits_to_state<MODEL, DT>(cbits, X[r][c], NE[r][c]);
+    }
+
+  uint32_t ca[4], cb[4];
+  if (nsteps > 0) {
+    fetch<DT>(A, B, M, N, K, bm, bn, 0, t, ca, cb);
+    produce<MODEL, DT>(&stage[0], ca, cb, t);
+  }
+  __syncthreads();
+
+  for (int64_t s = 0; s < nsteps; ++s) {
+    const Stage* st = &stage[s & 1];
+    const bool more = s + 1 < nsteps;
+    if (more) fetch<DT>(A, B, M, N, K, bm, bn, s + 1, t, ca, cb);
+
+    int S[4][4];
+    uint32_t mn[4][4];
+    int Xn[4][4];
+    uint32_t NEn[4][4];
+    bool bad = false;
+    if (MODEL == kAmpere) {
+      group<4, true>(st, ty, tx, 0, 0, NE, X, S, mn);
+      int X1[4][4];
+      uint32_t NE1[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          bad |= S[r][c] == 0;
+          normalise<0, F>(S[r][c], mn[r][c], X1[r][c], NE1[r][c]);
+        }
+      group<4, true>(st, ty, tx, 4, 1, NE1, X1, S, mn);
+    } else {
+      group<8, false>(st, ty, tx, 0, 0, NE, X, S, mn);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        normalise<F - 23, F>(S[r][c], mn[r][c], Xn[r][c], NEn[r][c]);
+        bad |= (S[r][c] == 0) | (NEn[r][c] - NE_OK_LO > NE_OK_SPAN);
+        // FP32 overflow: the state becomes inf (exponent above every product)
+        NEn[r][c] = NEn[r][c] <= NE_OVF ? C_INF : NEn[r][c];
+      }
+    if (bad) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          // recompute the whole 4x4 tile from the previous state
+          const uint2 v = slow_step<MODEL, DT>(st, 4 * ty + r, 4 * tx + c, X[r][c], NE[r][c]);
+          Xn[r][c] = (int)v.x;
+          NEn[r][c] = v.y;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        X[r][c] = Xn[r][c];
+        NE[r][c] = NEn[r][c];
+      }
+    if (more) produce<MODEL, DT>(&stage[(s + 1) & 1], ca, cb, t);
+    __syncthreads();
+  }
+
+  uint32_t rowx[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int64_t row = bm + 4 * ty + r, col = bn + 4 * tx + c;
+      const uint32_t d = state_to_bits<MODEL>(X[r][c], NE[r][c]);
+      if (row < M && col < N) {
+        D[row * N + col] = d;
+        rowx[r] ^= d;
+      }
+    }
+  if (xorsum) {
+    // XOR across the 16 lanes that share these rows (one 16-lane row of the wave)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      uint32_t v = rowx[r];
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) v ^= __shfl_xor(v, off, 16);
+      const int64_t row = bm + 4 * ty + r;
+      if (tx == 0 && row < M && v) atomicXor(&xorsum[row], v);
+    }
+  }
+}
+
+}  // namespace fastk
+
+inline bool gemm_fast_supported(int64_t M, int64_t N, int64_t K) {
+  return M > 0 && N > 0 && K >= 16 && (M + fastk::BM - 1) / fastk::BM <= 65535 &&
+         (N + fastk::BN - 1) / fastk::BN <= INT32_MAX;
+}
+
+template <int MODEL, int DT>
+inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, uint32_t* D,
+                             uint32_t* X, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  const dim3 grid((unsigned)((N + fastk::BN - 1) / fastk::BN),
+                  (unsigned)((M + fastk::BM - 1) / fastk::BM));
+  fastk::gemm_fast_kernel<MODEL, DT><<<grid, dim3(fastk::NT), 0, s>>>(A, B, C, D, X, M, N, K);
+}
+
 }  // namespace mmaemu
