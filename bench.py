@@ -46,6 +46,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU work for the oracle sample")
     p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="after the timed region, run a plain 256 MiB device copy twice "
+                        "(reference kernel for scaling HBM byte counters)")
     return p.parse_args()
 
 
@@ -120,6 +123,15 @@ def main():
     ev_total_s = sum(launch_ms) / 1e3
     ms_per_step = 1e3 * ev_total_s / args.steps
     value = MACS * args.steps / ev_total_s
+
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.int32, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # parity of the timed output against the oracle's full-output digest
     D = tD.cpu().numpy().view(np.uint32)
