@@ -13,6 +13,9 @@ HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-shared", "-fPIC",
     # no packed-FP32 instruction selection anywhere in this library
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # all packed 16-bit arithmetic in the kernels is explicit; the SLP
+    # vectoriser only pairs scalar epilogue ops at a net cost
+    "-fno-slp-vectorize",
     "-Wall", "-Wno-unused-function",
 ]
 

@@ -52,23 +52,34 @@ constexpr uint32_t NE_OK_LO = T_BIAS - 2047, NE_OK_SPAN = 2047 + 126;
 constexpr uint32_t NE_OVF = T_BIAS - 128;
 constexpr unsigned short SAT = 0xFFE0;
 
+// Rows are padded from 64 to 68 words: the producer writes 16-byte chunks
+// from 16 lanes that differ in k, which would otherwise all hit the same
+// banks; 68 keeps every row 16-byte aligned for the consumer's b128 reads.
+constexpr int PAD = BM + 4;
 struct Stage {
-  uint32_t a_val[16][BM];  // A significand << (F - 2t)
-  int32_t a_sgn[16][BM];   // 0 / -1
-  uint32_t a_ne[8][BM];    // NE of k = 2p | NE of k = 2p+1 << 16
-  uint32_t a_msk[2][BM];   // sign bits of the row's group products
-  int32_t b_val[16][BN];   // signed B significand
-  int32_t b_sgn[16][BN];
-  uint32_t b_ne[8][BN];
-  uint32_t b_msk[2][BN];
-  uint16_t a_raw[BM][16];  // raw codes for the per-output recompute
-  uint16_t b_raw[16][BN];
+  uint32_t a_val[16][PAD];  // A significand << (F - 2t)
+  int32_t a_sgn[16][PAD];   // 0 / -1
+  uint32_t a_ne[8][PAD];    // NE of k = 2p | NE of k = 2p+1 << 16
+  uint32_t a_msk[2][PAD];   // sign bits of the row's group products
+  int32_t b_val[16][PAD];   // signed B significand
+  int32_t b_sgn[16][PAD];
+  uint32_t b_ne[8][PAD];
+  uint32_t b_msk[2][PAD];
+  uint16_t a_raw[BM][16];   // raw codes for the per-output recompute
+  uint16_t b_raw[16][BN + 2];
 };
 
 __device__ __forceinline__ u16x2 as2(uint32_t x) { return __builtin_bit_cast(u16x2, x); }
 __device__ __forceinline__ uint32_t as32(u16x2 x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ u16x2 splat_lo(uint32_t x) {
   return u16x2{(unsigned short)x, (unsigned short)x};
+}
+// Leading zeros of x, and 0xFFFFFFFF for x = 0 (v_ffbh_u32 as is: __clz
+// would add a clamp for the zero case, which the callers never use).
+__device__ __forceinline__ uint32_t ffbh(uint32_t x) {
+  uint32_t r;
+  asm("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
 }
 // (a ^ b) + c in one VALU op (the compiler prefers xor + add3 pairs).
 __device__ __forceinline__ int xad(int a, int b, int c) {
@@ -281,8 +292,7 @@ __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, i
       K[r][c] = u16x2{SAT, SAT} - mn[r][c];
       // the extra term: one's complement significand, +1 if negative
       const u16x2 w = __builtin_elementwise_add_sat(splat_lo(ne_t[r][c]), K[r][c]);
-      const int X = X_t[r][c];
-      acc[r][c] = (X >> (as32(w) & 31)) - (X >> 31);
+      acc[r][c] = X_t[r][c] >> (as32(w) & 31);
     }
   // pass 2: products, truncating alignment, signed accumulation
 #pragma unroll
@@ -334,22 +344,27 @@ __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, i
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      S[r][c] = acc[r][c] + __popc(ma[r] ^ mb[c]);
+      // bit 31 carries the extra term's sign (the masks use at most 16 bits)
+      const uint32_t nm = (ma[r] ^ mb[c]) | ((uint32_t)X_t[r][c] & 0x80000000u);
+      S[r][c] = acc[r][c] + __popc(nm);
       mn_out[r][c] = as32(mn[r][c]);
     }
 }
 
 // Normalise a group sum: one's complement 24-bit significand (shifted by
 // extra bits onto the next group's grid) and its exponent code.
+// A zero S gives garbage here; callers flag S == 0 for the exact path.
+// NE is computed on the whole word: its low half is the exponent code
+// (mn's high half rides along unused).
 template <int EXTRA, int F>
 __device__ __forceinline__ void normalise(int S, uint32_t mn, int& X, uint32_t& NE) {
   const int s = S >> 31;
-  const uint32_t mag = (uint32_t)((S ^ s) - s);
-  const uint32_t lz = __clz(mag);
-  const uint32_t m = ((mag << lz) >> 8) << EXTRA;
+  const uint32_t mag = (uint32_t)max(S, -S);
+  const uint32_t lz = ffbh(mag);
+  const uint32_t m = ((mag << (lz & 31)) >> 8) << EXTRA;
   X = (int)m ^ s;
   // leading-bit exponent L = emax - F + 31 - lz  ->  NE = mn + F - 31 + lz
-  NE = (mn & 0xFFFFu) + (uint32_t)(F - 31) + lz;
+  NE = mn + lz + (uint32_t)(F - 31);
 }
 
 template <int MODEL, int DT>
@@ -411,9 +426,17 @@ __global__ __launch_bounds__(NT, 2) void gemm_fast_kernel(
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         normalise<F - 23, F>(S[r][c], mn[r][c], Xn[r][c], NEn[r][c]);
-        bad |= (S[r][c] == 0) | (NEn[r][c] - NE_OK_LO > NE_OK_SPAN);
-        // FP32 overflow: the state becomes inf (exponent above every product)
-        NEn[r][c] = NEn[r][c] <= NE_OVF ? C_INF : NEn[r][c];
+        const unsigned short ne16 = (unsigned short)NEn[r][c];
+        bad |= (S[r][c] == 0) | (ne16 < (unsigned short)NE_OK_LO) |
+               (ne16 > (unsigned short)(NE_OK_LO + NE_OK_SPAN));
+        // FP32 overflow (L >= 128): the state becomes inf.  FP16 and E4M3
+        // products stay below 2^33, so L = 128 already dominates them and a
+        // max suffices; BF16 products reach 2^256 and need E = 1024.
+        if (DT == kBF16) {
+          NEn[r][c] = ne16 <= NE_OVF ? C_INF : NEn[r][c];
+        } else {
+          NEn[r][c] = max(ne16, (unsigned short)NE_OVF);
+        }
       }
     if (bad) {
 #pragma unroll
