@@ -4,7 +4,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
+
+#include <mutex>
 
 #include "../../include/mmaemu.h"
 #include "mmaemu_common.h"
@@ -143,6 +146,44 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// Stream-ordered workspace for the operand pre-pass, from one memory pool
+// per device that keeps freed memory cached (release threshold = max), so
+// repeated calls do not go back to the driver.  A failed allocation is not
+// an error: the caller falls back to the kernel that unpacks in place.
+constexpr int kMaxDevices = 64;
+hipMemPool_t g_pool[kMaxDevices];
+std::once_flag g_pool_once[kMaxDevices];
+
+void* workspace_alloc(int64_t bytes, hipStream_t s) {
+  if (getenv("MMAEMU_NO_WORKSPACE")) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::call_once(g_pool_once[dev], [dev] {
+    hipMemPoolProps props;
+    memset(&props, 0, sizeof props);
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = dev;
+    if (hipMemPoolCreate(&g_pool[dev], &props) == hipSuccess) {
+      uint64_t keep = UINT64_MAX;
+      (void)hipMemPoolSetAttribute(g_pool[dev], hipMemPoolAttrReleaseThreshold, &keep);
+    } else {
+      g_pool[dev] = nullptr;
+      (void)hipGetLastError();
+    }
+  });
+  if (!g_pool[dev]) return nullptr;
+  void* p = nullptr;
+  if (hipMallocFromPoolAsync(&p, (size_t)bytes, g_pool[dev], s) != hipSuccess) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  return p;
+}
+
 template <int MODEL, int DT>
 hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, uint32_t* D,
                        uint32_t* X, int64_t M, int64_t N, int64_t K, hipStream_t s) {
@@ -151,7 +192,13 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, uint32_t
     fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(X, M);
   }
   if (gemm_fast_supported(M, N, K)) {
-    gemm_fast_launch<MODEL, DT>(A, B, C, D, X, M, N, K, s);
+    void* ws = workspace_alloc(gemm_fast_workspace_bytes(M, N, K), s);
+    gemm_fast_launch<MODEL, DT>(A, B, C, D, X, M, N, K, ws, s);
+    if (ws) {
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      (void)hipFreeAsync(ws, s);
+    }
   } else {
     const int64_t cb = (N + 255) / 256;
     const int64_t rows = M < 32768 ? M : 32768;

@@ -213,3 +213,34 @@ def test_gemm_full_size(torch_dev, orc, name):
         say("full size recompute", name)
         got2, gx2 = run_gemm(torch_dev, model, dt, A, B, C)
         assert np.array_equal(gx2, gx) and np.array_equal(got2, got)
+
+
+# --------------------------------------- the kernel that unpacks in place
+@pytest.fixture
+def no_workspace():
+    """Force the GEMM path that needs no pre-pass workspace (the library
+    reads MMAEMU_NO_WORKSPACE on every call)."""
+    os.environ["MMAEMU_NO_WORKSPACE"] = "1"
+    yield
+    del os.environ["MMAEMU_NO_WORKSPACE"]
+
+
+@pytest.mark.parametrize("model,dt", COMBOS)
+def test_gemm_in_place_unpack_path(torch_dev, orc, no_workspace, model, dt):
+    for kind in ("normal", "wide", "specials"):
+        for si, (M, N, K) in enumerate(SHAPES[2:]):
+            A, B, C = _gen(kind, model, dt, M, N, K, 2000 + si)
+            say("gemm (no workspace)", model, dt, kind, (M, N, K))
+            got, gx = run_gemm(torch_dev, model, dt, A, B, C)
+            want, wx = orc.gemm(model, dt, A, B, C)
+            assert_bits_equal(got, want, f"gemm/no-ws {model}/{dt}/{kind} {M}x{N}x{K}")
+            assert_bits_equal(gx, wx, f"gemm/no-ws xorsum {model}/{dt}/{kind} {M}x{N}x{K}")
+
+
+def test_gemm_full_size_in_place_unpack_path(torch_dev, no_workspace):
+    model, dt, gen = FULL["gemm_4096_fp16_ampere"]
+    A, B, C = gen()
+    say("full size (no workspace)", "gemm_4096_fp16_ampere")
+    got, gx = run_gemm(torch_dev, model, dt, A, B, C)
+    d = DIGESTS["gemm_4096_fp16_ampere"]
+    assert sha(got) == d["D_sha256"] and sha(gx) == d["xorsum_sha256"]
