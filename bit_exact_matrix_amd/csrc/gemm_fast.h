@@ -380,12 +380,39 @@ __global__ __launch_bounds__(64) void unpack_kernel(const void* __restrict__ src
   const int r = threadIdx.x;
   const int64_t idx = blk * 64 + r;
   OpImage* img = (OpImage*)(ws + (blk * nsteps + s) * IMG_WORDS);
+  uint32_t codes[16];
+  // an A row segment is 16 consecutive codes: two (or, for E4M3, one)
+  // 16-byte loads when the row start is 16-byte aligned
+  constexpr int esz = Fmt<DT>::bytes;
+  const bool vec = !IS_B && idx < limit &&
+                   (((uintptr_t)src | (uintptr_t)(K * esz)) & 15u) == 0;
+  if (vec) {
+    const uint4* p = (const uint4*)((const char*)src + (idx * K + 16 * s) * esz);
+    uint32_t w[8];
+    const uint4 v0 = p[0];
+    w[0] = v0.x, w[1] = v0.y, w[2] = v0.z, w[3] = v0.w;
+    if (esz == 2) {
+      const uint4 v1 = p[1];
+      w[4] = v1.x, w[5] = v1.y, w[6] = v1.z, w[7] = v1.w;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) codes[k] = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) codes[k] = (w[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      codes[k] = 0;
+      if (idx < limit)
+        codes[k] = IS_B ? load_code<DT>(src, (16 * s + k) * N + idx)
+                        : load_code<DT>(src, idx * K + 16 * s + k);
+    }
+  }
   uint32_t msk = 0, ne[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    uint32_t code = 0;
-    if (idx < limit)
-      code = IS_B ? load_code<DT>(src, (16 * s + k) * N + idx) : load_code<DT>(src, idx * K + 16 * s + k);
+    const uint32_t code = codes[k];
     uint32_t m;
     int sg;
     unpack<DT>(code, m, sg, ne[k]);
@@ -406,36 +433,99 @@ __global__ __launch_bounds__(64) void unpack_kernel(const void* __restrict__ src
 
 // Copy one step's A and B images (2 x 12 KiB) from the workspace into a
 // stage with direct global->LDS loads: 24 wave loads of 1 KiB, six per wave.
+// w is the wave index, already made wave-uniform, so that every address but
+// the lane offset stays in scalar registers.
 __device__ __forceinline__ void dma_step(Stage* st, const uint32_t* img_a, const uint32_t* img_b,
-                                         int t) {
-  const int w = t >> 6, lane = t & 63;
+                                         int w, int lane) {
 #pragma unroll
   for (int i = 0; i < 6; ++i) {
     const int kb = 6 * w + i;
-    const uint32_t* src = (kb < 12 ? img_a + kb * 256 : img_b + (kb - 12) * 256) + 4 * lane;
+    const uint32_t* base = kb < 12 ? img_a + kb * 256 : img_b + (kb - 12) * 256;
     __builtin_amdgcn_global_load_lds(
-        (const void*)src, (__attribute__((address_space(3))) void*)((uint32_t*)st + kb * 256),
-        16, 0, 0);
+        (const void*)(base + 4 * lane),
+        (__attribute__((address_space(3))) void*)((uint32_t*)st + kb * 256), 16, 0, 0);
+  }
+}
+
+// One chained MMA step for the lane's 4x4 outputs: state (X, NE) in,
+// (Xn, NEn) out.  Outputs whose fast result is not trustworthy (a zero group
+// sum, a result below FP32's normal range, an inf/NaN operand) are redone
+// exactly from the raw codes.
+template <int MODEL, int DT>
+__device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const void* A,
+                                          const void* B, int64_t M, int64_t N, int64_t K,
+                                          int64_t bm, int64_t bn, int64_t s,
+                                          const int (&X)[4][4], const uint32_t (&NE)[4][4],
+                                          int (&Xn)[4][4], uint32_t (&NEn)[4][4]) {
+  constexpr int F = Model<MODEL>::F;
+  int S[4][4];
+  uint32_t mn[4][4];
+  bool bad = false;
+  if (MODEL == kAmpere) {
+    group<4, true>(st, ty, tx, 0, 0, NE, X, S, mn);
+    int X1[4][4];
+    uint32_t NE1[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        bad |= S[r][c] == 0;
+        normalise<0, F>(S[r][c], mn[r][c], X1[r][c], NE1[r][c]);
+      }
+    group<4, true>(st, ty, tx, 4, 1, NE1, X1, S, mn);
+  } else {
+    group<8, false>(st, ty, tx, 0, 0, NE, X, S, mn);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      normalise<F - 23, F>(S[r][c], mn[r][c], Xn[r][c], NEn[r][c]);
+      const unsigned short ne16 = (unsigned short)NEn[r][c];
+      bad |= (S[r][c] == 0) | (ne16 < (unsigned short)NE_OK_LO) |
+             (ne16 > (unsigned short)(NE_OK_LO + NE_OK_SPAN));
+      // FP32 overflow (L >= 128): the state becomes inf.  FP16 and E4M3
+      // products stay below 2^33, so L = 128 already dominates them and a
+      // max suffices; BF16 products reach 2^256 and need E = 1024.
+      if (DT == kBF16) {
+        NEn[r][c] = ne16 <= NE_OVF ? C_INF : NEn[r][c];
+      } else {
+        NEn[r][c] = max(ne16, (unsigned short)NE_OVF);
+      }
+    }
+  if (bad) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        // recompute the whole 4x4 tile from the previous state
+        const uint2 v = slow_step<MODEL, DT>(A, B, M, N, K, bm + 4 * ty + r, bn + 4 * tx + c, s,
+                                             X[r][c], NE[r][c]);
+        Xn[r][c] = (int)v.x;
+        NEn[r][c] = v.y;
+      }
   }
 }
 
 // DMA = true: the operand images come from the pre-pass workspace (ws_a,
 // ws_b) by direct global->LDS copies; DMA = false: the kernel unpacks the
-// raw codes itself (no workspace).
+// raw codes itself (no workspace).  The K loop is unrolled twice so that the
+// accumulator state alternates between two register sets instead of being
+// copied back every step.
 template <int MODEL, int DT, bool DMA>
 __global__ __launch_bounds__(NT, 2) void gemm_fast_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, uint32_t* D,
     uint32_t* __restrict__ xorsum, int64_t M, int64_t N, int64_t K,
     const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b) {
-  constexpr int F = Model<MODEL>::F;
   __shared__ Stage stage[2];
   const int t = threadIdx.x;
   const int ty = t >> 4, tx = t & 15;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int64_t bm = (int64_t)blockIdx.y * BM, bn = (int64_t)blockIdx.x * BN;
   const int64_t nsteps = K / 16;
 
-  int X[4][4];
-  uint32_t NE[4][4];
+  int X[4][4], Xn[4][4];
+  uint32_t NE[4][4], NEn[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -448,89 +538,46 @@ __global__ __launch_bounds__(NT, 2) void gemm_fast_kernel(
   const uint32_t* img_a = DMA ? ws_a + (int64_t)blockIdx.y * nsteps * IMG_WORDS : nullptr;
   const uint32_t* img_b = DMA ? ws_b + (int64_t)blockIdx.x * nsteps * IMG_WORDS : nullptr;
   uint32_t ca[4], cb[4];
-  if (nsteps > 0) {
+  // stage s of the K walk: start the fill of stage s+1, compute, finish the fill
+  auto begin_fill = [&](int64_t s) {
     if constexpr (DMA) {
-      dma_step(&stage[0], img_a, img_b, t);
+      dma_step(&stage[s & 1], img_a + s * IMG_WORDS, img_b + s * IMG_WORDS, w, lane);
+    } else {
+      fetch<DT>(A, B, M, N, K, bm, bn, s, t, ca, cb);
+    }
+  };
+  auto end_fill = [&](int64_t s) {
+    if constexpr (DMA) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-      fetch<DT>(A, B, M, N, K, bm, bn, 0, t, ca, cb);
-      produce<MODEL, DT>(&stage[0], ca, cb, t);
+      produce<MODEL, DT>(&stage[s & 1], ca, cb, t);
     }
+  };
+  if (nsteps > 0) {
+    begin_fill(0);
+    end_fill(0);
   }
   __syncthreads();
 
-  for (int64_t s = 0; s < nsteps; ++s) {
-    const Stage* st = &stage[s & 1];
-    const bool more = s + 1 < nsteps;
-    if (more) {
-      if constexpr (DMA) {
-        dma_step(&stage[(s + 1) & 1], img_a + (s + 1) * IMG_WORDS, img_b + (s + 1) * IMG_WORDS, t);
-      } else {
-        fetch<DT>(A, B, M, N, K, bm, bn, s + 1, t, ca, cb);
-      }
-    }
-
-    int S[4][4];
-    uint32_t mn[4][4];
-    int Xn[4][4];
-    uint32_t NEn[4][4];
-    bool bad = false;
-    if (MODEL == kAmpere) {
-      group<4, true>(st, ty, tx, 0, 0, NE, X, S, mn);
-      int X1[4][4];
-      uint32_t NE1[4][4];
+  for (int64_t s = 0; s < nsteps; s += 2) {
+    if (s + 1 < nsteps) begin_fill(s + 1);
+    tile_step<MODEL, DT>(&stage[s & 1], ty, tx, A, B, M, N, K, bm, bn, s, X, NE, Xn, NEn);
+    if (s + 1 < nsteps) end_fill(s + 1);
+    __syncthreads();
+    if (s + 1 >= nsteps) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          bad |= S[r][c] == 0;
-          normalise<0, F>(S[r][c], mn[r][c], X1[r][c], NE1[r][c]);
+          X[r][c] = Xn[r][c];
+          NE[r][c] = NEn[r][c];
         }
-      group<4, true>(st, ty, tx, 4, 1, NE1, X1, S, mn);
-    } else {
-      group<8, false>(st, ty, tx, 0, 0, NE, X, S, mn);
+      break;
     }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        normalise<F - 23, F>(S[r][c], mn[r][c], Xn[r][c], NEn[r][c]);
-        const unsigned short ne16 = (unsigned short)NEn[r][c];
-        bad |= (S[r][c] == 0) | (ne16 < (unsigned short)NE_OK_LO) |
-               (ne16 > (unsigned short)(NE_OK_LO + NE_OK_SPAN));
-        // FP32 overflow (L >= 128): the state becomes inf.  FP16 and E4M3
-        // products stay below 2^33, so L = 128 already dominates them and a
-        // max suffices; BF16 products reach 2^256 and need E = 1024.
-        if (DT == kBF16) {
-          NEn[r][c] = ne16 <= NE_OVF ? C_INF : NEn[r][c];
-        } else {
-          NEn[r][c] = max(ne16, (unsigned short)NE_OVF);
-        }
-      }
-    if (bad) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          // recompute the whole 4x4 tile from the previous state
-          const uint2 v = slow_step<MODEL, DT>(A, B, M, N, K, bm + 4 * ty + r, bn + 4 * tx + c,
-                                               s, X[r][c], NE[r][c]);
-          Xn[r][c] = (int)v.x;
-          NEn[r][c] = v.y;
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        X[r][c] = Xn[r][c];
-        NE[r][c] = NEn[r][c];
-      }
-    if constexpr (DMA) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-      if (more) produce<MODEL, DT>(&stage[(s + 1) & 1], ca, cb, t);
-    }
+    if (s + 2 < nsteps) begin_fill(s + 2);
+    tile_step<MODEL, DT>(&stage[(s + 1) & 1], ty, tx, A, B, M, N, K, bm, bn, s + 1, Xn, NEn, X,
+                         NE);
+    if (s + 2 < nsteps) end_fill(s + 2);
     __syncthreads();
   }
 
