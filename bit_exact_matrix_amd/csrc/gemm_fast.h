@@ -7,25 +7,32 @@
 //    register tile and walks the K/16 chained MMA steps, carrying its 16
 //    accumulators in registers in a decoded form (no FP32 pack/unpack per
 //    step);
-//  * per step the workgroup loads the 64x16 A slice and 16x64 B slice once
-//    (raw codes, coalesced) and unpacks them into LDS (double-buffered):
-//    A: significand pre-shifted onto the group grid, sign mask, exponent;
-//    B: signed significand, sign mask, exponent; plus per-row / per-column
-//    sign bitmasks for the group;
-//  * exponents live as 16-bit "negated biased" values NE = bias - E, two per
-//    register, so one packed add gives the exponents of two products and one
-//    packed min their running maximum (pass 1); a saturating packed add of
-//    NE - min + 0xFFE0 then yields both alignment distances already clamped
-//    to 31 in their low 5 bits (the shifter only reads 5 bits);
+//  * each K-step the workgroup needs the 64x16 A slice and the 16x64 B slice
+//    as "operand images" in LDS (double-buffered): A significands
+//    pre-shifted onto the group grid, B significands signed, sign masks,
+//    16-bit exponent codes and per-row / per-column sign bitmasks.  The
+//    images are either built once per GEMM by a pre-pass into a workspace
+//    and copied with direct global->LDS loads, or built in the kernel from
+//    the raw codes when no workspace is available;
+//  * exponents are 16-bit "negated biased" codes NE = bias - E, two per
+//    register, paired by OUTPUT (rows 2r and 2r+1 of the lane tile): one
+//    packed add gives the exponents of two products, one packed min keeps
+//    the running maximum of two outputs (pass 1), and a saturating packed
+//    add of NE - min + 0xFFE0 yields both alignment distances already
+//    clamped to 31 in their low 5 bits (the shifter reads 5 bits);
 //  * pass 2 per product: v_mad_i32_i24 forms the exact product in one's
 //    complement of B's sign (b*a + sb = m ^ sb), an arithmetic shift by the
 //    clamped distance truncates the MAGNITUDE toward zero
 //    (asr(m ^ s, d) = (m >> d) ^ s), and v_xad_u32 applies A's sign and
 //    accumulates; the +1 owed by every negative term is added once per
 //    group as a popcount of the XOR of the two sign bitmasks;
-//  * every rare case -- a zero group sum, an FP32-subnormal result, an inf
-//    or NaN operand -- is detected with a range check and recomputed for
-//    that output alone by step_generic from the raw codes kept in LDS.
+//  * a group sum of zero gets the exponent code 0xFFFF (a saturating add of
+//    the leading-zero count, which is all ones for zero): as an Ampere
+//    stage-1 term it then takes no part in stage 2, as a final result it
+//    fails the range check;
+//  * every rare case -- a zero result, an FP32-subnormal result, an inf or
+//    NaN operand -- fails a range check and the lane's tile is recomputed
+//    for that step by step_generic from the raw codes.
 #pragma once
 
 #include "mmaemu_common.h"
@@ -57,12 +64,14 @@ constexpr unsigned short SAT = 0xFFE0;
 // from lanes that differ in k, which would otherwise all hit the same banks;
 // 68 keeps every row 16-byte aligned for the b128 reads.  The image is
 // 12 KiB so that it can also be copied from HBM in whole 1 KiB wave loads.
+//   ne, A image: word [p][2q + j] = NE of rows (2q, 2q+1) at k = 2p + j
+//   ne, B image: word [p][c]      = NE of column c at k = 2p | k = 2p+1
 constexpr int PAD = BM + 4;
 constexpr int IMG_WORDS = 3072;
 struct OpImage {
   uint32_t val[16][PAD];  // A: significand << (F - 2t); B: signed significand
   int32_t sgn[16][PAD];   // 0 / -1
-  uint32_t ne[8][PAD];    // NE of k = 2p | NE of k = 2p+1 << 16
+  uint32_t ne[8][PAD];    // exponent codes, two per word (see above)
   uint32_t msk[2][PAD];   // sign bits of the row's / column's group products
   uint32_t pad_[IMG_WORDS - 42 * PAD];
 };
@@ -76,8 +85,14 @@ __device__ __forceinline__ uint32_t as32(u16x2 x) { return __builtin_bit_cast(ui
 __device__ __forceinline__ u16x2 splat_lo(uint32_t x) {
   return u16x2{(unsigned short)x, (unsigned short)x};
 }
+__device__ __forceinline__ u16x2 splat_hi(uint32_t x) {
+  return u16x2{(unsigned short)(x >> 16), (unsigned short)(x >> 16)};
+}
+__device__ __forceinline__ unsigned short half16(uint32_t x, int h) {
+  return (unsigned short)(h ? x >> 16 : x);
+}
 // Leading zeros of x, and 0xFFFFFFFF for x = 0 (v_ffbh_u32 as is: __clz
-// would add a clamp for the zero case, which the callers never use).
+// would add a clamp for the zero case).
 __device__ __forceinline__ uint32_t ffbh(uint32_t x) {
   uint32_t r;
   asm("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(x));
@@ -104,17 +119,23 @@ __device__ __forceinline__ void unpack(uint32_t code, uint32_t& m, int& s, uint3
   m = sub ? frac : (frac | (1u << F::t));
   const int E = sub ? 1 - F::bias : (int)ef - F::bias;
   ne = special ? OP_SPECIAL : (m == 0 ? OP_ZERO : (uint32_t)((int)OP_BIAS - E));
-  if (special) m = 0;
+  // Zero and inf/NaN operands carry a dummy nonzero significand.  A product
+  // with a zero operand sits thousands of binades below every real term, so
+  // it is always shifted out, and a group made of nothing else lands out of
+  // range.  A product with an inf/NaN operand (inf * 0 included) then never
+  // sums to exactly zero: its huge exponent cannot be mistaken for an empty
+  // Ampere stage-1 sum and always reaches the range check.
+  if (special || m == 0) m = 1u << F::t;
 }
 
 // Accumulator state <-> FP32 bits.  X = M ^ s with M the significand on
-// the group grid (24 bits, << (F-23)); NE = 0x4000 - E in the low half.
-template <int MODEL, int DT>
-__device__ __forceinline__ void bits_to_state(uint32_t bits, int& X, uint32_t& NE) {
+// the group grid (24 bits, << (F-23)); ne = 0x4000 - E (16 bits).
+template <int MODEL>
+__device__ __forceinline__ void bits_to_state(uint32_t bits, int& X, uint32_t& ne) {
   constexpr int F = Model<MODEL>::F;
   const int s = (int)bits >> 31;
   const uint32_t ef = (bits >> 23) & 0xFFu, fr = bits & 0x7FFFFFu;
-  uint32_t m, ne;
+  uint32_t m;
   if (ef == 0xFFu) {
     m = 0x800000u;
     ne = fr ? C_NAN : C_INF;
@@ -126,16 +147,15 @@ __device__ __forceinline__ void bits_to_state(uint32_t bits, int& X, uint32_t& N
     ne = (uint32_t)(T_BIAS - ((int)ef - 127));
   }
   X = (int)(m << (F - 23)) ^ s;
-  NE = ne;
 }
 
 template <int MODEL>
-__device__ __forceinline__ uint32_t state_to_bits(int X, uint32_t NE) {
+__device__ __forceinline__ uint32_t state_to_bits(int X, uint32_t ne) {
   constexpr int F = Model<MODEL>::F;
   const int s = X >> 31;
   const uint32_t sign = (uint32_t)s & 0x80000000u;
   const uint32_t m = (uint32_t)(X ^ s) >> (F - 23);
-  const uint32_t ne = NE & 0xFFFFu;
+  ne &= 0xFFFFu;
   if (ne == C_NAN) return kNaN;
   if (ne == C_ZERO) return sign;
   const int E = T_BIAS - (int)ne;
@@ -149,64 +169,61 @@ __device__ __forceinline__ uint32_t state_to_bits(int X, uint32_t NE) {
 template <int MODEL, int DT>
 __device__ __noinline__ uint2 slow_step(const void* A, const void* B, int64_t M, int64_t N,
                                         int64_t K, int64_t row, int64_t col, int64_t s,
-                                        int Xold, uint32_t NEold) {
+                                        int Xold, uint32_t ne_old) {
   uint32_t a[16], b[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     a[k] = row < M ? load_code<DT>(A, row * K + 16 * s + k) : 0u;
     b[k] = col < N ? load_code<DT>(B, (16 * s + k) * N + col) : 0u;
   }
-  const uint32_t c = state_to_bits<MODEL>(Xold, NEold);
+  const uint32_t c = state_to_bits<MODEL>(Xold, ne_old);
   const uint32_t r = step_generic<MODEL, DT>(c, a, b);
   int X;
-  uint32_t NE;
-  bits_to_state<MODEL, DT>(r, X, NE);
-  return make_uint2((uint32_t)X, NE);
+  uint32_t ne;
+  bits_to_state<MODEL>(r, X, ne);
+  return make_uint2((uint32_t)X, ne);
 }
 
+// Operand image contents of one element, A side and B side.
+template <int MODEL, int DT>
+__device__ __forceinline__ void image_a(uint32_t code, uint32_t& val, int& sgn, uint32_t& ne) {
+  constexpr int pshift = Model<MODEL>::F - 2 * Fmt<DT>::t;
+  uint32_t m;
+  unpack<DT>(code, m, sgn, ne);
+  val = m << pshift;
+}
 template <int DT>
-__device__ __forceinline__ uint32_t ld_code(const void* p, int64_t idx) {
-  return load_code<DT>(p, idx);
+__device__ __forceinline__ void image_b(uint32_t code, uint32_t& val, int& sgn, uint32_t& ne) {
+  uint32_t m;
+  unpack<DT>(code, m, sgn, ne);
+  val = (uint32_t)(sgn ? -(int)m : (int)m);
 }
 
-// Unpack this lane's share of the next step into stage st: lane
-// (k = t & 15, q = t >> 4) handles A rows 4q..4q+3 and B cols 4q..4q+3 at k.
+// In-kernel image builder (no workspace): lane (k = t & 15, q = t >> 4)
+// handles A rows 4q..4q+3 and B cols 4q..4q+3 at k.
 template <int MODEL, int DT>
 __device__ __forceinline__ void produce(Stage* st, const uint32_t (&ca)[4],
                                         const uint32_t (&cb)[4], int t) {
-  constexpr int F = Model<MODEL>::F;
-  constexpr int pshift = F - 2 * Fmt<DT>::t;
   const int k = t & 15, q = t >> 4;
-  uint32_t av[4], ane[4], bne[4];
-  int as[4], bv[4], bs[4];
+  uint32_t av[4], ane[4], bv[4], bne[4];
+  int as[4], bs[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    uint32_t m, ne;
-    int s;
-    unpack<DT>(ca[u], m, s, ne);
-    av[u] = m << pshift;
-    as[u] = s;
-    ane[u] = ne;
-    unpack<DT>(cb[u], m, s, ne);
-    bv[u] = s ? -(int)m : (int)m;
-    bs[u] = s;
-    bne[u] = ne;
+    image_a<MODEL, DT>(ca[u], av[u], as[u], ane[u]);
+    image_b<DT>(cb[u], bv[u], bs[u], bne[u]);
   }
   *(uint4*)&st->a.val[k][4 * q] = make_uint4(av[0], av[1], av[2], av[3]);
   *(int4*)&st->a.sgn[k][4 * q] = make_int4(as[0], as[1], as[2], as[3]);
-  *(int4*)&st->b.val[k][4 * q] = make_int4(bv[0], bv[1], bv[2], bv[3]);
+  *(uint4*)&st->b.val[k][4 * q] = make_uint4(bv[0], bv[1], bv[2], bv[3]);
   *(int4*)&st->b.sgn[k][4 * q] = make_int4(bs[0], bs[1], bs[2], bs[3]);
-  // exponent pairs (k even, k odd): the partner is the adjacent lane
-  uint32_t pa[4], pb[4];
+  // A exponents: rows paired within the lane
+  st->a.ne[k >> 1][4 * q + (k & 1)] = ane[0] | ane[1] << 16;
+  st->a.ne[k >> 1][4 * q + 2 + (k & 1)] = ane[2] | ane[3] << 16;
+  // B exponents: k paired with the adjacent lane
+  uint32_t pb[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    pa[u] = __shfl_xor(ane[u], 1, 64);
-    pb[u] = __shfl_xor(bne[u], 1, 64);
-  }
+  for (int u = 0; u < 4; ++u) pb[u] = __shfl_xor(bne[u], 1, 64);
   if ((k & 1) == 0) {
-    *(uint4*)&st->a.ne[k >> 1][4 * q] =
-        make_uint4(ane[0] | pa[0] << 16, ane[1] | pa[1] << 16, ane[2] | pa[2] << 16,
-                   ane[3] | pa[3] << 16);
     *(uint4*)&st->b.ne[k >> 1][4 * q] =
         make_uint4(bne[0] | pb[0] << 16, bne[1] | pb[1] << 16, bne[2] | pb[2] << 16,
                    bne[3] | pb[3] << 16);
@@ -214,23 +231,21 @@ __device__ __forceinline__ void produce(Stage* st, const uint32_t (&ca)[4],
   // sign bitmasks: a ballot over the wave gives, for each 16-lane group,
   // the 16 sign bits (k = 0..15) of one row / column
   const int g = (t & 63) >> 4;
-  uint32_t am[4], bm[4];
+  uint32_t am[4], bmk[4];
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const uint64_t ba = __ballot(as[u] != 0);
-    const uint64_t bb = __ballot(bs[u] != 0);
-    am[u] = (uint32_t)(ba >> (16 * g)) & 0xFFFFu;
-    bm[u] = (uint32_t)(bb >> (16 * g)) & 0xFFFFu;
+    am[u] = (uint32_t)(__ballot(as[u] != 0) >> (16 * g)) & 0xFFFFu;
+    bmk[u] = (uint32_t)(__ballot(bs[u] != 0) >> (16 * g)) & 0xFFFFu;
   }
   if (k == 0) {
     if (MODEL == kAmpere) {
       *(uint4*)&st->a.msk[0][4 * q] = make_uint4(am[0] & 0xFF, am[1] & 0xFF, am[2] & 0xFF, am[3] & 0xFF);
       *(uint4*)&st->a.msk[1][4 * q] = make_uint4(am[0] >> 8, am[1] >> 8, am[2] >> 8, am[3] >> 8);
-      *(uint4*)&st->b.msk[0][4 * q] = make_uint4(bm[0] & 0xFF, bm[1] & 0xFF, bm[2] & 0xFF, bm[3] & 0xFF);
-      *(uint4*)&st->b.msk[1][4 * q] = make_uint4(bm[0] >> 8, bm[1] >> 8, bm[2] >> 8, bm[3] >> 8);
+      *(uint4*)&st->b.msk[0][4 * q] = make_uint4(bmk[0] & 0xFF, bmk[1] & 0xFF, bmk[2] & 0xFF, bmk[3] & 0xFF);
+      *(uint4*)&st->b.msk[1][4 * q] = make_uint4(bmk[0] >> 8, bmk[1] >> 8, bmk[2] >> 8, bmk[3] >> 8);
     } else {
       *(uint4*)&st->a.msk[0][4 * q] = make_uint4(am[0], am[1], am[2], am[3]);
-      *(uint4*)&st->b.msk[0][4 * q] = make_uint4(bm[0], bm[1], bm[2], bm[3]);
+      *(uint4*)&st->b.msk[0][4 * q] = make_uint4(bmk[0], bmk[1], bmk[2], bmk[3]);
     }
   }
 }
@@ -245,137 +260,20 @@ __device__ __forceinline__ void fetch(const void* A, const void* B, int64_t M, i
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int64_t row = bm + 4 * q + u;
-    ca[u] = row < M ? ld_code<DT>(A, row * K + kk) : 0u;
+    ca[u] = row < M ? load_code<DT>(A, row * K + kk) : 0u;
     const int64_t col = bn + 4 * q + u;
-    cb[u] = col < N ? ld_code<DT>(B, kk * N + col) : 0u;
+    cb[u] = col < N ? load_code<DT>(B, kk * N + col) : 0u;
   }
 }
 
-// One group of products for the lane's 4x4 outputs.
-//   p0, np: first pair and pair count of the group.
-//   ne_t / X_t: the group's extra term (C, or the Ampere stage-1 sum).
-// Returns S (signed exact group sum on the grid of the group's emax) and
-// mn (= 0x4000 - emax, both halves).
-template <int NP, bool STORE_ES>
-__device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, int gmask,
-                                      const uint32_t (&ne_t)[4][4], const int (&X_t)[4][4],
-                                      int (&S)[4][4], uint32_t (&mn_out)[4][4]) {
-  u16x2 mn[4][4];
-  u16x2 es[STORE_ES ? NP : 1][4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) mn[r][c] = splat_lo(ne_t[r][c]);
-  // pass 1: exponents of every product and their running maximum
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const uint4 a4 = *(const uint4*)&st->a.ne[p0 + p][4 * ty];
-    const uint4 b4 = *(const uint4*)&st->b.ne[p0 + p][4 * tx];
-    const uint32_t a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const u16x2 e = as2(a[r]) + as2(b[c]);
-        if constexpr (STORE_ES) es[p][r][c] = e;
-        mn[r][c] = __builtin_elementwise_min(mn[r][c], e);
-      }
-  }
-  u16x2 K[4][4];
-  int acc[4][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      mn[r][c] = __builtin_elementwise_min(mn[r][c], mn[r][c].yx);
-      K[r][c] = u16x2{SAT, SAT} - mn[r][c];
-      // the extra term: one's complement significand, +1 if negative
-      const u16x2 w = __builtin_elementwise_add_sat(splat_lo(ne_t[r][c]), K[r][c]);
-      acc[r][c] = X_t[r][c] >> (as32(w) & 31);
-    }
-  // pass 2: products, truncating alignment, signed accumulation
-#pragma unroll
-  for (int p = 0; p < NP; ++p) {
-    const int k0 = 2 * (p0 + p), k1 = k0 + 1;
-    const uint4 av0 = *(const uint4*)&st->a.val[k0][4 * ty];
-    const uint4 av1 = *(const uint4*)&st->a.val[k1][4 * ty];
-    const int4 as0 = *(const int4*)&st->a.sgn[k0][4 * ty];
-    const int4 as1 = *(const int4*)&st->a.sgn[k1][4 * ty];
-    const int4 bv0 = *(const int4*)&st->b.val[k0][4 * tx];
-    const int4 bv1 = *(const int4*)&st->b.val[k1][4 * tx];
-    const int4 bs0 = *(const int4*)&st->b.sgn[k0][4 * tx];
-    const int4 bs1 = *(const int4*)&st->b.sgn[k1][4 * tx];
-    const uint32_t a0[4] = {av0.x, av0.y, av0.z, av0.w}, a1[4] = {av1.x, av1.y, av1.z, av1.w};
-    const int sa0[4] = {as0.x, as0.y, as0.z, as0.w}, sa1[4] = {as1.x, as1.y, as1.z, as1.w};
-    const int b0[4] = {bv0.x, bv0.y, bv0.z, bv0.w}, b1[4] = {bv1.x, bv1.y, bv1.z, bv1.w};
-    const int sb0[4] = {bs0.x, bs0.y, bs0.z, bs0.w}, sb1[4] = {bs1.x, bs1.y, bs1.z, bs1.w};
-    uint32_t ane[4] = {0, 0, 0, 0}, bne[4] = {0, 0, 0, 0};
-    if constexpr (!STORE_ES) {
-      const uint4 a4 = *(const uint4*)&st->a.ne[p0 + p][4 * ty];
-      const uint4 b4 = *(const uint4*)&st->b.ne[p0 + p][4 * tx];
-      ane[0] = a4.x, ane[1] = a4.y, ane[2] = a4.z, ane[3] = a4.w;
-      bne[0] = b4.x, bne[1] = b4.y, bne[2] = b4.z, bne[3] = b4.w;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        u16x2 e;
-        if constexpr (STORE_ES) {
-          e = es[p][r][c];
-        } else {
-          e = as2(ane[r]) + as2(bne[c]);
-        }
-        const uint32_t w = as32(__builtin_elementwise_add_sat(e, K[r][c]));
-        const int x0 = __mul24(b0[c], (int)a0[r]) + sb0[c];
-        const int x1 = __mul24(b1[c], (int)a1[r]) + sb1[c];
-        const int t0 = x0 >> (w & 31);
-        const int t1 = x1 >> ((w >> 16) & 31);
-        acc[r][c] = xad(t0, sa0[r], acc[r][c]);
-        acc[r][c] = xad(t1, sa1[r], acc[r][c]);
-      }
-  }
-  // +1 for every negative product: popcount of the XOR of the sign masks
-  const uint4 am = *(const uint4*)&st->a.msk[gmask][4 * ty];
-  const uint4 bmk = *(const uint4*)&st->b.msk[gmask][4 * tx];
-  const uint32_t ma[4] = {am.x, am.y, am.z, am.w}, mb[4] = {bmk.x, bmk.y, bmk.z, bmk.w};
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      // bit 31 carries the extra term's sign (the masks use at most 16 bits)
-      const uint32_t nm = (ma[r] ^ mb[c]) | ((uint32_t)X_t[r][c] & 0x80000000u);
-      S[r][c] = acc[r][c] + __popc(nm);
-      mn_out[r][c] = as32(mn[r][c]);
-    }
-}
-
-// Normalise a group sum: one's complement 24-bit significand (shifted by
-// extra bits onto the next group's grid) and its exponent code.
-// A zero S gives garbage here; callers flag S == 0 for the exact path.
-// NE is computed on the whole word: its low half is the exponent code
-// (mn's high half rides along unused).
-template <int EXTRA, int F>
-__device__ __forceinline__ void normalise(int S, uint32_t mn, int& X, uint32_t& NE) {
-  const int s = S >> 31;
-  const uint32_t mag = (uint32_t)max(S, -S);
-  const uint32_t lz = ffbh(mag);
-  const uint32_t m = ((mag << (lz & 31)) >> 8) << EXTRA;
-  X = (int)m ^ s;
-  // leading-bit exponent L = emax - F + 31 - lz  ->  NE = mn + F - 31 + lz
-  NE = mn + lz + (uint32_t)(F - 31);
-}
-
-// Pre-pass: unpack one operand once per GEMM into per-(block, step) images
-// (workspace layout [block][step][OpImage]), so the GEMM kernel only copies
-// them into LDS.  One 64-lane workgroup per (step, block); lane r owns row r
-// of an A block (IS_B false) or column r of a B block (IS_B true).
+// Pre-pass: build one operand's images once per GEMM (workspace layout
+// [block][step][OpImage]), so the GEMM kernel only copies them into LDS.
+// One 64-lane workgroup per (step, block); lane r owns row r of an A block
+// (IS_B false) or column r of a B block (IS_B true).
 template <int MODEL, int DT, bool IS_B>
 __global__ __launch_bounds__(64) void unpack_kernel(const void* __restrict__ src, int64_t limit,
                                                     int64_t K, int64_t N, int64_t nsteps,
                                                     uint32_t* __restrict__ ws) {
-  constexpr int F = Model<MODEL>::F;
-  constexpr int pshift = F - 2 * Fmt<DT>::t;
   const int64_t s = blockIdx.x, blk = blockIdx.y;
   const int r = threadIdx.x;
   const int64_t idx = blk * 64 + r;
@@ -412,16 +310,30 @@ __global__ __launch_bounds__(64) void unpack_kernel(const void* __restrict__ src
   uint32_t msk = 0, ne[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    const uint32_t code = codes[k];
-    uint32_t m;
+    uint32_t val;
     int sg;
-    unpack<DT>(code, m, sg, ne[k]);
-    img->val[k][r] = IS_B ? (uint32_t)(sg ? -(int)m : (int)m) : (m << pshift);
+    if (IS_B) {
+      image_b<DT>(codes[k], val, sg, ne[k]);
+    } else {
+      image_a<MODEL, DT>(codes[k], val, sg, ne[k]);
+    }
+    img->val[k][r] = val;
     img->sgn[k][r] = sg;
     msk |= (uint32_t)(sg & 1) << k;
   }
+  if (IS_B) {
 #pragma unroll
-  for (int p = 0; p < 8; ++p) img->ne[p][r] = ne[2 * p] | ne[2 * p + 1] << 16;
+    for (int p = 0; p < 8; ++p) img->ne[p][r] = ne[2 * p] | ne[2 * p + 1] << 16;
+  } else {
+    // rows (r & ~1, r | 1) share a word; lane r writes k = 2p + (r & 1),
+    // taking the other row's code from its partner lane r ^ 1
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const uint32_t mine = (r & 1) ? ne[2 * p + 1] : ne[2 * p];
+      const uint32_t other = __shfl_xor((r & 1) ? ne[2 * p] : ne[2 * p + 1], 1, 64);
+      img->ne[p][r] = (r & 1) ? (other | mine << 16) : (mine | other << 16);
+    }
+  }
   if (MODEL == kAmpere) {
     img->msk[0][r] = msk & 0xFFu;
     img->msk[1][r] = msk >> 8;
@@ -447,71 +359,200 @@ __device__ __forceinline__ void dma_step(Stage* st, const uint32_t* img_a, const
   }
 }
 
-// One chained MMA step for the lane's 4x4 outputs: state (X, NE) in,
-// (Xn, NEn) out.  Outputs whose fast result is not trustworthy (a zero group
-// sum, a result below FP32's normal range, an inf/NaN operand) are redone
-// exactly from the raw codes.
-template <int MODEL, int DT>
-__device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const void* A,
-                                          const void* B, int64_t M, int64_t N, int64_t K,
-                                          int64_t bm, int64_t bn, int64_t s,
-                                          const int (&X)[4][4], const uint32_t (&NE)[4][4],
-                                          int (&Xn)[4][4], uint32_t (&NEn)[4][4]) {
-  constexpr int F = Model<MODEL>::F;
-  int S[4][4];
-  uint32_t mn[4][4];
-  bool bad = false;
-  if (MODEL == kAmpere) {
-    group<4, true>(st, ty, tx, 0, 0, NE, X, S, mn);
-    int X1[4][4];
-    uint32_t NE1[4][4];
+// One group of products for the lane's 4x4 outputs.
+//   p0, NP: first k-pair and k-pair count of the group; gmask: sign-mask row.
+//   ne_t / X_t: the group's extra term (C, or the Ampere stage-1 sum), its
+//   exponent codes paired by output (rows 2q, 2q+1).
+// Returns S (signed exact group sum on the grid of the group's emax) and
+// mn (= 0x4000 - emax, paired like ne_t).
+template <int NP, bool STORE_ES>
+__device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, int gmask,
+                                      const uint32_t (&ne_t)[2][4], const int (&X_t)[4][4],
+                                      int (&S)[4][4], uint32_t (&mn_out)[2][4]) {
+  u16x2 mn[2][4];
+  u16x2 es[STORE_ES ? 2 * NP : 1][2][4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        bad |= S[r][c] == 0;
-        normalise<0, F>(S[r][c], mn[r][c], X1[r][c], NE1[r][c]);
-      }
-    group<4, true>(st, ty, tx, 4, 1, NE1, X1, S, mn);
-  } else {
-    group<8, false>(st, ty, tx, 0, 0, NE, X, S, mn);
+    for (int c = 0; c < 4; ++c) mn[q][c] = as2(ne_t[q][c]);
+  // pass 1: exponents of every product and the running maximum per output
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    const uint4 a4 = *(const uint4*)&st->a.ne[p0 + p][4 * ty];
+    const uint4 b4 = *(const uint4*)&st->b.ne[p0 + p][4 * tx];
+    const uint32_t a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const u16x2 e = as2(a[2 * q + j]) + (j ? splat_hi(b[c]) : splat_lo(b[c]));
+          if constexpr (STORE_ES) es[2 * p + j][q][c] = e;
+          mn[q][c] = __builtin_elementwise_min(mn[q][c], e);
+        }
   }
+  u16x2 K[2][4];
+  int acc[4][4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      K[q][c] = u16x2{SAT, SAT} - mn[q][c];
+      // the extra term: one's complement significand shifted onto the grid
+      const uint32_t w = as32(__builtin_elementwise_add_sat(as2(ne_t[q][c]), K[q][c]));
+      acc[2 * q][c] = X_t[2 * q][c] >> (w & 31);
+      acc[2 * q + 1][c] = X_t[2 * q + 1][c] >> ((w >> 16) & 31);
+    }
+  // pass 2: products, truncating alignment, signed accumulation
+#pragma unroll
+  for (int p = 0; p < NP; ++p) {
+    uint32_t ane[4] = {0, 0, 0, 0}, bne[4] = {0, 0, 0, 0};
+    if constexpr (!STORE_ES) {
+      const uint4 a4 = *(const uint4*)&st->a.ne[p0 + p][4 * ty];
+      const uint4 b4 = *(const uint4*)&st->b.ne[p0 + p][4 * tx];
+      ane[0] = a4.x, ane[1] = a4.y, ane[2] = a4.z, ane[3] = a4.w;
+      bne[0] = b4.x, bne[1] = b4.y, bne[2] = b4.z, bne[3] = b4.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int k = 2 * (p0 + p) + j;
+      const uint4 av = *(const uint4*)&st->a.val[k][4 * ty];
+      const int4 as = *(const int4*)&st->a.sgn[k][4 * ty];
+      const int4 bv = *(const int4*)&st->b.val[k][4 * tx];
+      const int4 bs = *(const int4*)&st->b.sgn[k][4 * tx];
+      const uint32_t a[4] = {av.x, av.y, av.z, av.w};
+      const int sa[4] = {as.x, as.y, as.z, as.w};
+      const int b[4] = {bv.x, bv.y, bv.z, bv.w};
+      const int sb[4] = {bs.x, bs.y, bs.z, bs.w};
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u16x2 e;
+          if constexpr (STORE_ES) {
+            e = es[2 * p + j][q][c];
+          } else {
+            e = as2(ane[2 * q + j]) + (j ? splat_hi(bne[c]) : splat_lo(bne[c]));
+          }
+          const uint32_t w = as32(__builtin_elementwise_add_sat(e, K[q][c]));
+          const int r0 = 2 * q, r1 = 2 * q + 1;
+          const int x0 = __mul24(b[c], (int)a[r0]) + sb[c];
+          const int x1 = __mul24(b[c], (int)a[r1]) + sb[c];
+          const int t0 = x0 >> (w & 31);
+          const int t1 = x1 >> ((w >> 16) & 31);
+          acc[r0][c] = xad(t0, sa[r0], acc[r0][c]);
+          acc[r1][c] = xad(t1, sa[r1], acc[r1][c]);
+        }
+    }
+  }
+  // +1 for every negative term: popcount of the XOR of the sign masks, with
+  // the extra term's sign in bit 31 (the masks use at most 16 bits)
+  const uint4 am = *(const uint4*)&st->a.msk[gmask][4 * ty];
+  const uint4 bmk = *(const uint4*)&st->b.msk[gmask][4 * tx];
+  const uint32_t ma[4] = {am.x, am.y, am.z, am.w}, mb[4] = {bmk.x, bmk.y, bmk.z, bmk.w};
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      normalise<F - 23, F>(S[r][c], mn[r][c], Xn[r][c], NEn[r][c]);
-      const unsigned short ne16 = (unsigned short)NEn[r][c];
-      bad |= (S[r][c] == 0) | (ne16 < (unsigned short)NE_OK_LO) |
-             (ne16 > (unsigned short)(NE_OK_LO + NE_OK_SPAN));
+      const uint32_t nm = (ma[r] ^ mb[c]) | ((uint32_t)X_t[r][c] & 0x80000000u);
+      S[r][c] = acc[r][c] + __popc(nm);
+    }
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) mn_out[q][c] = as32(mn[q][c]);
+}
+
+// Normalise the group sums of two outputs (one exponent pair): one's
+// complement 24-bit significands (shifted by EXTRA onto the next group's
+// grid) and their exponent codes L = emax - F + 31 - lz, i.e.
+// NE = mn + (F - 31) + lz, by a saturating add so that a zero sum (lz all
+// ones) gets 0xFFFF.
+template <int EXTRA, int F>
+__device__ __forceinline__ void normalise2(int S0, int S1, uint32_t mn, int& X0, int& X1,
+                                           uint32_t& NE) {
+  const int s0 = S0 >> 31, s1 = S1 >> 31;
+  const uint32_t m0 = (uint32_t)max(S0, -S0), m1 = (uint32_t)max(S1, -S1);
+  const uint32_t lz0 = ffbh(m0), lz1 = ffbh(m1);
+  X0 = (int)(((m0 << (lz0 & 31)) >> 8) << EXTRA) ^ s0;
+  X1 = (int)(((m1 << (lz1 & 31)) >> 8) << EXTRA) ^ s1;
+  const uint32_t lz = __builtin_amdgcn_perm(lz1, lz0, 0x05040100u);  // lz0 | lz1 << 16
+  const u16x2 base = as2(mn) - u16x2{(unsigned short)(31 - F), (unsigned short)(31 - F)};
+  NE = as32(__builtin_elementwise_add_sat(as2(lz), base));
+}
+
+// One chained MMA step for the lane's 4x4 outputs: state (X, NE) in,
+// (Xn, NEn) out.  Outputs whose fast result is not trustworthy (a zero
+// result, a result below FP32's normal range, an inf/NaN operand) are redone
+// exactly from the raw codes, for the whole lane tile.
+template <int MODEL, int DT>
+__device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const void* A,
+                                          const void* B, int64_t M, int64_t N, int64_t K,
+                                          int64_t bm, int64_t bn, int64_t s,
+                                          const int (&X)[4][4], const uint32_t (&NE)[2][4],
+                                          int (&Xn)[4][4], uint32_t (&NEn)[2][4]) {
+  constexpr int F = Model<MODEL>::F;
+  int S[4][4];
+  uint32_t mn[2][4];
+  if (MODEL == kAmpere) {
+    group<4, true>(st, ty, tx, 0, 0, NE, X, S, mn);
+    int X1[4][4];
+    uint32_t NE1[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        normalise2<0, F>(S[2 * q][c], S[2 * q + 1][c], mn[q][c], X1[2 * q][c],
+                         X1[2 * q + 1][c], NE1[q][c]);
+    group<4, true>(st, ty, tx, 4, 1, NE1, X1, S, mn);
+  } else {
+    group<8, false>(st, ty, tx, 0, 0, NE, X, S, mn);
+  }
+  bool bad = false;
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      normalise2<F - 23, F>(S[2 * q][c], S[2 * q + 1][c], mn[q][c], Xn[2 * q][c],
+                            Xn[2 * q + 1][c], NEn[q][c]);
+      const uint32_t ne = NEn[q][c];
+      bad |= ((unsigned short)(ne - NE_OK_LO) > NE_OK_SPAN) |
+             ((unsigned short)((ne >> 16) - NE_OK_LO) > NE_OK_SPAN);
       // FP32 overflow (L >= 128): the state becomes inf.  FP16 and E4M3
       // products stay below 2^33, so L = 128 already dominates them and a
       // max suffices; BF16 products reach 2^256 and need E = 1024.
       if (DT == kBF16) {
-        NEn[r][c] = ne16 <= NE_OVF ? C_INF : NEn[r][c];
+        const uint32_t lo = (ne & 0xFFFFu) <= NE_OVF ? C_INF : (ne & 0xFFFFu);
+        const uint32_t hi = (ne >> 16) <= NE_OVF ? C_INF : (ne >> 16);
+        NEn[q][c] = lo | hi << 16;
       } else {
-        NEn[r][c] = max(ne16, (unsigned short)NE_OVF);
+        NEn[q][c] = as32(__builtin_elementwise_max(
+            as2(ne), u16x2{(unsigned short)NE_OVF, (unsigned short)NE_OVF}));
       }
     }
   if (bad) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         // recompute the whole 4x4 tile from the previous state
-        const uint2 v = slow_step<MODEL, DT>(A, B, M, N, K, bm + 4 * ty + r, bn + 4 * tx + c, s,
-                                             X[r][c], NE[r][c]);
-        Xn[r][c] = (int)v.x;
-        NEn[r][c] = v.y;
+        const uint2 v0 = slow_step<MODEL, DT>(A, B, M, N, K, bm + 4 * ty + 2 * q, bn + 4 * tx + c,
+                                              s, X[2 * q][c], NE[q][c] & 0xFFFFu);
+        const uint2 v1 = slow_step<MODEL, DT>(A, B, M, N, K, bm + 4 * ty + 2 * q + 1,
+                                              bn + 4 * tx + c, s, X[2 * q + 1][c], NE[q][c] >> 16);
+        Xn[2 * q][c] = (int)v0.x;
+        Xn[2 * q + 1][c] = (int)v1.x;
+        NEn[q][c] = v0.y | v1.y << 16;
       }
   }
 }
 
 // DMA = true: the operand images come from the pre-pass workspace (ws_a,
-// ws_b) by direct global->LDS copies; DMA = false: the kernel unpacks the
-// raw codes itself (no workspace).  The K loop is unrolled twice so that the
-// accumulator state alternates between two register sets instead of being
-// copied back every step.
+// ws_b) by direct global->LDS copies; DMA = false: the kernel builds them
+// from the raw codes (no workspace).  The K loop is unrolled twice so that
+// the accumulator state alternates between two register sets instead of
+// being copied back every step.
 template <int MODEL, int DT, bool DMA>
 __global__ __launch_bounds__(NT, 2) void gemm_fast_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, uint32_t* D,
@@ -525,20 +566,25 @@ __global__ __launch_bounds__(NT, 2) void gemm_fast_kernel(
   const int64_t nsteps = K / 16;
 
   int X[4][4], Xn[4][4];
-  uint32_t NE[4][4], NEn[4][4];
+  uint32_t NE[2][4], NEn[2][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int64_t row = bm + 4 * ty + r, col = bn + 4 * tx + c;
-      const uint32_t cbits = (C && row < M && col < N) ? C[row * N + col] : 0u;
-      bits_to_state<MODEL, DT>(cbits, X[r][c], NE[r][c]);
+      uint32_t ne[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int64_t row = bm + 4 * ty + 2 * q + h, col = bn + 4 * tx + c;
+        const uint32_t cbits = (C && row < M && col < N) ? C[row * N + col] : 0u;
+        bits_to_state<MODEL>(cbits, X[2 * q + h][c], ne[h]);
+      }
+      NE[q][c] = ne[0] | ne[1] << 16;
     }
 
   const uint32_t* img_a = DMA ? ws_a + (int64_t)blockIdx.y * nsteps * IMG_WORDS : nullptr;
   const uint32_t* img_b = DMA ? ws_b + (int64_t)blockIdx.x * nsteps * IMG_WORDS : nullptr;
   uint32_t ca[4], cb[4];
-  // stage s of the K walk: start the fill of stage s+1, compute, finish the fill
+  // fill of stage s: start it (before the previous step's compute), end it
   auto begin_fill = [&](int64_t s) {
     if constexpr (DMA) {
       dma_step(&stage[s & 1], img_a + s * IMG_WORDS, img_b + s * IMG_WORDS, w, lane);
@@ -568,10 +614,11 @@ __global__ __launch_bounds__(NT, 2) void gemm_fast_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          X[r][c] = Xn[r][c];
-          NE[r][c] = NEn[r][c];
-        }
+        for (int c = 0; c < 4; ++c) X[r][c] = Xn[r][c];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) NE[q][c] = NEn[q][c];
       break;
     }
     if (s + 2 < nsteps) begin_fill(s + 2);
@@ -587,7 +634,7 @@ __global__ __launch_bounds__(NT, 2) void gemm_fast_kernel(
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int64_t row = bm + 4 * ty + r, col = bn + 4 * tx + c;
-      const uint32_t d = state_to_bits<MODEL>(X[r][c], NE[r][c]);
+      const uint32_t d = state_to_bits<MODEL>(X[r][c], half16(NE[r >> 1][c], r & 1));
       if (row < M && col < N) {
         D[row * N + col] = d;
         rowx[r] ^= d;
@@ -619,7 +666,7 @@ inline int64_t gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (mb + nb) * (K / 16) * (int64_t)sizeof(fastk::OpImage);
 }
 
-// ws: NULL for the in-kernel unpack, else gemm_fast_workspace_bytes() bytes.
+// ws: NULL for the in-kernel image build, else gemm_fast_workspace_bytes() bytes.
 template <int MODEL, int DT>
 inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, uint32_t* D,
                              uint32_t* X, int64_t M, int64_t N, int64_t K, void* ws,
