@@ -98,6 +98,15 @@ __device__ __forceinline__ uint32_t ffbh(uint32_t x) {
   asm("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(x));
   return r;
 }
+// Minimum of three pairs of 16-bit exponent codes.  Every code that reaches
+// it is a positive normal binary16 bit pattern (0x0800 .. 0x6000), and for
+// those the binary16 order is the integer order, so the packed binary16
+// minimum3 folds two products' exponents per instruction.
+__device__ __forceinline__ u16x2 min3h(u16x2 a, u16x2 b, u16x2 c) {
+  uint32_t r;
+  asm("v_pk_minimum3_f16 %0, %1, %2, %3" : "=v"(r) : "v"(as32(a)), "v"(as32(b)), "v"(as32(c)));
+  return as2(r);
+}
 // (a ^ b) + c in one VALU op (the compiler prefers xor + add3 pairs).
 __device__ __forceinline__ int xad(int a, int b, int c) {
   int r;
@@ -363,9 +372,11 @@ __device__ __forceinline__ void dma_step(Stage* st, const uint32_t* img_a, const
 //   p0, NP: first k-pair and k-pair count of the group; gmask: sign-mask row.
 //   ne_t / X_t: the group's extra term (C, or the Ampere stage-1 sum), its
 //   exponent codes paired by output (rows 2q, 2q+1).
+// NT_EMPTY: the extra term may be an empty sum (code 0xFFFF, a binary16 NaN
+// pattern), which then goes through an integer min.
 // Returns S (signed exact group sum on the grid of the group's emax) and
 // mn (= 0x4000 - emax, paired like ne_t).
-template <int NP, bool STORE_ES>
+template <int NP, bool STORE_ES, bool NT_EMPTY>
 __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, int gmask,
                                       const uint32_t (&ne_t)[2][4], const int (&X_t)[4][4],
                                       int (&S)[4][4], uint32_t (&mn_out)[2][4]) {
@@ -375,6 +386,7 @@ __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, i
   for (int q = 0; q < 2; ++q)
 #pragma unroll
     for (int c = 0; c < 4; ++c) mn[q][c] = as2(ne_t[q][c]);
+  static_assert(STORE_ES || !NT_EMPTY, "an empty extra term needs the stored exponents");
   // pass 1: exponents of every product and the running maximum per output
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
@@ -382,15 +394,28 @@ __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, i
     const uint4 b4 = *(const uint4*)&st->b.ne[p0 + p][4 * tx];
     const uint32_t a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int q = 0; q < 2; ++q)
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const u16x2 e = as2(a[2 * q + j]) + (j ? splat_hi(b[c]) : splat_lo(b[c]));
-          if constexpr (STORE_ES) es[2 * p + j][q][c] = e;
-          mn[q][c] = __builtin_elementwise_min(mn[q][c], e);
+      for (int c = 0; c < 4; ++c) {
+        const u16x2 e0 = as2(a[2 * q]) + splat_lo(b[c]);
+        const u16x2 e1 = as2(a[2 * q + 1]) + splat_hi(b[c]);
+        if constexpr (STORE_ES) {
+          es[2 * p][q][c] = e0;
+          es[2 * p + 1][q][c] = e1;
         }
+        if constexpr (!NT_EMPTY) mn[q][c] = min3h(mn[q][c], e0, e1);
+      }
+  }
+  if constexpr (NT_EMPTY) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        u16x2 m = __builtin_elementwise_min(mn[q][c], es[0][q][c]);
+#pragma unroll
+        for (int i = 1; i + 1 < 2 * NP; i += 2) m = min3h(m, es[i][q][c], es[i + 1][q][c]);
+        mn[q][c] = __builtin_elementwise_min(m, es[2 * NP - 1][q][c]);
+      }
   }
   u16x2 K[2][4];
   int acc[4][4];
@@ -496,7 +521,7 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
   int S[4][4];
   uint32_t mn[2][4];
   if (MODEL == kAmpere) {
-    group<4, true>(st, ty, tx, 0, 0, NE, X, S, mn);
+    group<4, true, false>(st, ty, tx, 0, 0, NE, X, S, mn);
     int X1[4][4];
     uint32_t NE1[2][4];
 #pragma unroll
@@ -505,11 +530,12 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
       for (int c = 0; c < 4; ++c)
         normalise2<0, F>(S[2 * q][c], S[2 * q + 1][c], mn[q][c], X1[2 * q][c],
                          X1[2 * q + 1][c], NE1[q][c]);
-    group<4, true>(st, ty, tx, 4, 1, NE1, X1, S, mn);
+    group<4, true, true>(st, ty, tx, 4, 1, NE1, X1, S, mn);
   } else {
-    group<8, false>(st, ty, tx, 0, 0, NE, X, S, mn);
+    group<8, false, false>(st, ty, tx, 0, 0, NE, X, S, mn);
   }
-  bool bad = false;
+  // range check: the largest (NE - NE_OK_LO) mod 2^16 over the 16 outputs
+  u16x2 rng = {0, 0};
 #pragma unroll
   for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -517,8 +543,8 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
       normalise2<F - 23, F>(S[2 * q][c], S[2 * q + 1][c], mn[q][c], Xn[2 * q][c],
                             Xn[2 * q + 1][c], NEn[q][c]);
       const uint32_t ne = NEn[q][c];
-      bad |= ((unsigned short)(ne - NE_OK_LO) > NE_OK_SPAN) |
-             ((unsigned short)((ne >> 16) - NE_OK_LO) > NE_OK_SPAN);
+      rng = __builtin_elementwise_max(
+          rng, as2(ne) - u16x2{(unsigned short)NE_OK_LO, (unsigned short)NE_OK_LO});
       // FP32 overflow (L >= 128): the state becomes inf.  FP16 and E4M3
       // products stay below 2^33, so L = 128 already dominates them and a
       // max suffices; BF16 products reach 2^256 and need E = 1024.
@@ -531,7 +557,7 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
             as2(ne), u16x2{(unsigned short)NE_OVF, (unsigned short)NE_OVF}));
       }
     }
-  if (bad) {
+  if ((rng.x > NE_OK_SPAN) | (rng.y > NE_OK_SPAN)) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
