@@ -368,33 +368,56 @@ __device__ __forceinline__ void dma_step(Stage* st, const uint32_t* img_a, const
   }
 }
 
-// One group of products for the lane's 4x4 outputs.
+// Words [4*ty + 2*QB, 4*ty + 2*(QB + QN)) of an LDS row: the values of
+// the lane's row pairs QB .. QB+QN-1 (or, in the exponent rows of the A
+// image, their pair words), placed at their own indices of v.
+template <int QB, int QN, typename T>
+__device__ __forceinline__ void lds_pairs(const T* row, int ty, T (&v)[4]) {
+  static_assert(QN == 2 || (QN == 1 && QB < 2), "one or both row pairs");
+  if constexpr (QN == 2) {
+    const uint4 x = *(const uint4*)&row[4 * ty];
+    v[0] = (T)x.x, v[1] = (T)x.y, v[2] = (T)x.z, v[3] = (T)x.w;
+  } else {
+    const uint2 x = *(const uint2*)&row[4 * ty + 2 * QB];
+    v[2 * QB] = (T)x.x, v[2 * QB + 1] = (T)x.y;
+  }
+}
+template <typename T>
+__device__ __forceinline__ void lds_quad(const T* row, int tx, T (&v)[4]) {
+  const uint4 x = *(const uint4*)&row[4 * tx];
+  v[0] = (T)x.x, v[1] = (T)x.y, v[2] = (T)x.z, v[3] = (T)x.w;
+}
+
+// One group of products for the outputs of row pairs QB .. QB+QN-1 of the
+// lane's 4x4 tile (rows 2q, 2q+1 form pair q).
 //   p0, NP: first k-pair and k-pair count of the group; gmask: sign-mask row.
 //   ne_t / X_t: the group's extra term (C, or the Ampere stage-1 sum), its
 //   exponent codes paired by output (rows 2q, 2q+1).
 // NT_EMPTY: the extra term may be an empty sum (code 0xFFFF, a binary16 NaN
 // pattern), which then goes through an integer min.
+// STORE_ES keeps every product exponent of pass 1 in registers (2*NP*QN*4
+// of them) for pass 2; otherwise pass 2 recomputes them.
 // Returns S (signed exact group sum on the grid of the group's emax) and
-// mn (= 0x4000 - emax, paired like ne_t).
-template <int NP, bool STORE_ES, bool NT_EMPTY>
+// mn (= 0x4000 - emax, paired like ne_t) for the pairs it covers.
+template <int NP, bool STORE_ES, bool NT_EMPTY, int QB = 0, int QN = 2>
 __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, int gmask,
                                       const uint32_t (&ne_t)[2][4], const int (&X_t)[4][4],
                                       int (&S)[4][4], uint32_t (&mn_out)[2][4]) {
+  static_assert(STORE_ES || !NT_EMPTY, "an empty extra term needs the stored exponents");
   u16x2 mn[2][4];
   u16x2 es[STORE_ES ? 2 * NP : 1][2][4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = QB; q < QB + QN; ++q)
 #pragma unroll
     for (int c = 0; c < 4; ++c) mn[q][c] = as2(ne_t[q][c]);
-  static_assert(STORE_ES || !NT_EMPTY, "an empty extra term needs the stored exponents");
   // pass 1: exponents of every product and the running maximum per output
 #pragma unroll
   for (int p = 0; p < NP; ++p) {
-    const uint4 a4 = *(const uint4*)&st->a.ne[p0 + p][4 * ty];
-    const uint4 b4 = *(const uint4*)&st->b.ne[p0 + p][4 * tx];
-    const uint32_t a[4] = {a4.x, a4.y, a4.z, a4.w}, b[4] = {b4.x, b4.y, b4.z, b4.w};
+    uint32_t a[4], b[4];
+    lds_pairs<QB, QN>(st->a.ne[p0 + p], ty, a);
+    lds_quad(st->b.ne[p0 + p], tx, b);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = QB; q < QB + QN; ++q)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const u16x2 e0 = as2(a[2 * q]) + splat_lo(b[c]);
@@ -408,7 +431,7 @@ __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, i
   }
   if constexpr (NT_EMPTY) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = QB; q < QB + QN; ++q)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         u16x2 m = __builtin_elementwise_min(mn[q][c], es[0][q][c]);
@@ -420,7 +443,7 @@ __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, i
   u16x2 K[2][4];
   int acc[4][4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = QB; q < QB + QN; ++q)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       K[q][c] = u16x2{SAT, SAT} - mn[q][c];
@@ -434,24 +457,20 @@ __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, i
   for (int p = 0; p < NP; ++p) {
     uint32_t ane[4] = {0, 0, 0, 0}, bne[4] = {0, 0, 0, 0};
     if constexpr (!STORE_ES) {
-      const uint4 a4 = *(const uint4*)&st->a.ne[p0 + p][4 * ty];
-      const uint4 b4 = *(const uint4*)&st->b.ne[p0 + p][4 * tx];
-      ane[0] = a4.x, ane[1] = a4.y, ane[2] = a4.z, ane[3] = a4.w;
-      bne[0] = b4.x, bne[1] = b4.y, bne[2] = b4.z, bne[3] = b4.w;
+      lds_pairs<QB, QN>(st->a.ne[p0 + p], ty, ane);
+      lds_quad(st->b.ne[p0 + p], tx, bne);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int k = 2 * (p0 + p) + j;
-      const uint4 av = *(const uint4*)&st->a.val[k][4 * ty];
-      const int4 as = *(const int4*)&st->a.sgn[k][4 * ty];
-      const int4 bv = *(const int4*)&st->b.val[k][4 * tx];
-      const int4 bs = *(const int4*)&st->b.sgn[k][4 * tx];
-      const uint32_t a[4] = {av.x, av.y, av.z, av.w};
-      const int sa[4] = {as.x, as.y, as.z, as.w};
-      const int b[4] = {bv.x, bv.y, bv.z, bv.w};
-      const int sb[4] = {bs.x, bs.y, bs.z, bs.w};
+      uint32_t a[4];
+      int sa[4], b[4], sb[4];
+      lds_pairs<QB, QN>(st->a.val[k], ty, a);
+      lds_pairs<QB, QN>(st->a.sgn[k], ty, sa);
+      lds_quad((const int*)st->b.val[k], tx, b);
+      lds_quad(st->b.sgn[k], tx, sb);
 #pragma unroll
-      for (int q = 0; q < 2; ++q)
+      for (int q = QB; q < QB + QN; ++q)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           u16x2 e;
@@ -473,18 +492,18 @@ __device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, i
   }
   // +1 for every negative term: popcount of the XOR of the sign masks, with
   // the extra term's sign in bit 31 (the masks use at most 16 bits)
-  const uint4 am = *(const uint4*)&st->a.msk[gmask][4 * ty];
-  const uint4 bmk = *(const uint4*)&st->b.msk[gmask][4 * tx];
-  const uint32_t ma[4] = {am.x, am.y, am.z, am.w}, mb[4] = {bmk.x, bmk.y, bmk.z, bmk.w};
+  uint32_t ma[4], mb[4];
+  lds_pairs<QB, QN>(st->a.msk[gmask], ty, ma);
+  lds_quad(st->b.msk[gmask], tx, mb);
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 2 * QB; r < 2 * (QB + QN); ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const uint32_t nm = (ma[r] ^ mb[c]) | ((uint32_t)X_t[r][c] & 0x80000000u);
       S[r][c] = acc[r][c] + __popc(nm);
     }
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = QB; q < QB + QN; ++q)
 #pragma unroll
     for (int c = 0; c < 4; ++c) mn_out[q][c] = as32(mn[q][c]);
 }
@@ -520,24 +539,10 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
   constexpr int F = Model<MODEL>::F;
   int S[4][4];
   uint32_t mn[2][4];
-  if (MODEL == kAmpere) {
-    group<4, true, false>(st, ty, tx, 0, 0, NE, X, S, mn);
-    int X1[4][4];
-    uint32_t NE1[2][4];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        normalise2<0, F>(S[2 * q][c], S[2 * q + 1][c], mn[q][c], X1[2 * q][c],
-                         X1[2 * q + 1][c], NE1[q][c]);
-    group<4, true, true>(st, ty, tx, 4, 1, NE1, X1, S, mn);
-  } else {
-    group<8, false, false>(st, ty, tx, 0, 0, NE, X, S, mn);
-  }
   // range check: the largest (NE - NE_OK_LO) mod 2^16 over the 16 outputs
   u16x2 rng = {0, 0};
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
+  // final normalisation, range check and overflow snap of row pair q
+  auto finish = [&](int q) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       normalise2<F - 23, F>(S[2 * q][c], S[2 * q + 1][c], mn[q][c], Xn[2 * q][c],
@@ -557,6 +562,31 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
             as2(ne), u16x2{(unsigned short)NE_OVF, (unsigned short)NE_OVF}));
       }
     }
+  };
+  if (MODEL == kAmpere) {
+    group<4, true, false>(st, ty, tx, 0, 0, NE, X, S, mn);
+    int X1[4][4];
+    uint32_t NE1[2][4];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        normalise2<0, F>(S[2 * q][c], S[2 * q + 1][c], mn[q][c], X1[2 * q][c],
+                         X1[2 * q + 1][c], NE1[q][c]);
+    group<4, true, true>(st, ty, tx, 4, 1, NE1, X1, S, mn);
+    finish(0);
+    finish(1);
+  } else {
+    // one row pair at a time: the 16 product exponents of 8 outputs stay in
+    // 64 registers
+    group<8, true, false, 0, 1>(st, ty, tx, 0, 0, NE, X, S, mn);
+    finish(0);
+    // reload the B operands from LDS for the second pair rather than keep
+    // all 16 k-steps of them live across the first
+    asm volatile("" ::: "memory");
+    group<8, true, false, 1, 1>(st, ty, tx, 0, 0, NE, X, S, mn);
+    finish(1);
+  }
   if ((rng.x > NE_OK_SPAN) | (rng.y > NE_OK_SPAN)) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
@@ -574,13 +604,21 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
   }
 }
 
+// Waves per SIMD the register allocation is sized for.  A step keeps 64
+// product exponents in registers (an Ampere group over the whole tile, a
+// Hopper group over half of it) and fits three; its only spills sit around
+// the rare recompute calls.  The in-kernel image build needs more registers
+// and stays at two.
+template <int MODEL, bool DMA>
+constexpr int kWavesPerSimd = DMA ? 3 : 2;
+
 // DMA = true: the operand images come from the pre-pass workspace (ws_a,
 // ws_b) by direct global->LDS copies; DMA = false: the kernel builds them
 // from the raw codes (no workspace).  The K loop is unrolled twice so that
 // the accumulator state alternates between two register sets instead of
 // being copied back every step.
 template <int MODEL, int DT, bool DMA>
-__global__ __launch_bounds__(NT, 2) void gemm_fast_kernel(
+__global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, uint32_t* D,
     uint32_t* __restrict__ xorsum, int64_t M, int64_t N, int64_t K,
     const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b) {
