@@ -23,13 +23,17 @@ sys.path.insert(0, ROOT)
 
 M = N = K = 4096
 MACS = M * N * K
-# Algorithmic integer operations per emulated MAC of the Ampere FP16 model:
-# exact product, exponent add, max, distance, truncating shift, signed add
-# (6 per MAC) plus the per-group normalisation and the per-step FP32
-# write-back amortised over 8 and 16 MACs (about 1 per MAC).
-ALG_OPS_PER_MAC = 7
+# Algorithmic integer work per emulated MAC of the Ampere FP16 model, in
+# 32-bit VALU issue slots (the unit of the peak below).  Per MAC: the exact
+# product, the truncating alignment shift and the signed accumulate (one
+# slot each), and the exponent add, running maximum and alignment distance
+# on exponents that fit 16 bits (half a slot each: two per 32-bit lane) =
+# 4.5.  Per output and 16-MAC step: two group-sum normalisations (about 6
+# slots each: magnitude, leading-bit search, 24-bit truncating shift, sign,
+# exponent) and the FP32 range test of the result (1) = 13/16 per MAC.
+ALG_SLOTS_PER_MAC = 4.5 + 13 / 16
 # MI355X integer VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one
-# 32-bit integer operation per lane per clock (non-packed).
+# 32-bit lane operation per lane per clock.
 VALU_PEAK_OPS = 256 * 64 * 2.4e9
 # The pages' CPU simulator on the same workload: 50.8 s for 4096^3 on an
 # Apple M4 Pro (Hawkeye notes, "Experiments and results", Table 1).
@@ -52,16 +56,16 @@ def parse():
     return p.parse_args()
 
 
-def traffic_record(kernel_hash):
-    """HBM bytes per launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "gemm_4096_fp16_ampere_hbm_traffic.json")
+def profile_record(name, kernel_hash):
+    """A committed rocprofv3 counter summary under profiles/, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("kernel_source_sha256") != kernel_hash:
         return None
-    return rec.get("bytes_per_launch")
+    return rec
 
 
 def kernel_source_hash():
@@ -109,7 +113,8 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: K steps bracketed by synchronisation; HIP events on the
-    # launch stream give the per-launch durations
+    # launch stream give the per-launch durations (one launch = the operand
+    # pre-pass and the GEMM kernel, which takes about 99% of it)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -142,15 +147,23 @@ def main():
                  and hashlib.sha256(X.tobytes()).hexdigest() == ref.get("xorsum_sha256"))
 
     avg_launch_s = ev_total_s / args.steps
-    achieved = ALG_OPS_PER_MAC * MACS / avg_launch_s
+    achieved = ALG_SLOTS_PER_MAC * MACS / avg_launch_s
     khash = kernel_source_hash()
-    traffic = traffic_record(khash)
+    hbm = profile_record("gemm_4096_fp16_ampere_hbm_traffic.json", khash)
+    valu = profile_record("gemm_4096_fp16_ampere_valu_counters.json", khash)
     roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3),
                 "peak": round(VALU_PEAK_OPS / 1e12, 3), "unit": "TOP/s",
-                "frac": round(achieved / VALU_PEAK_OPS, 4), "traffic": traffic,
-                "ops_per_mac": ALG_OPS_PER_MAC,
+                "frac": round(achieved / VALU_PEAK_OPS, 4),
+                "traffic": hbm["bytes_per_launch"] if hbm else None,
+                "alg_slots_per_mac": ALG_SLOTS_PER_MAC,
                 "launch_ms_mean": round(1e3 * avg_launch_s, 4),
                 "launch_ms_min": round(min(launch_ms), 4)}
+    if valu:
+        # executed VALU lane operations (rocprofv3 SQ_INSTS_VALU x 64 for this
+        # kernel source) over the live launch time: the VALU share of peak
+        roofline["valu_slots_per_mac"] = valu["valu_slots_per_mac"]
+        roofline["valu_frac"] = round(
+            valu["valu_slots_per_mac"] * MACS / avg_launch_s / VALU_PEAK_OPS, 4)
 
     cpu = None
     if not args.no_cpu_baseline:

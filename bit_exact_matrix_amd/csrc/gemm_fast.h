@@ -174,11 +174,16 @@ __device__ __forceinline__ uint32_t state_to_bits(int X, uint32_t ne) {
 }
 
 // Recompute one output's step from the raw codes in global memory (rare
-// path).  Rows and columns outside the matrix read as +0 codes.
+// path): output (r, c) of the calling lane's 4x4 tile in the workgroup's
+// 64x64 block.  Rows and columns outside the matrix read as +0 codes.  The
+// row and column are derived here rather than passed, so that the caller
+// keeps no per-lane 64-bit indices live across its loop.
 template <int MODEL, int DT>
 __device__ __noinline__ uint2 slow_step(const void* A, const void* B, int64_t M, int64_t N,
-                                        int64_t K, int64_t row, int64_t col, int64_t s,
-                                        int Xold, uint32_t ne_old) {
+                                        int64_t K, int64_t s, int tr, int tc, int Xold,
+                                        uint32_t ne_old) {
+  const int64_t row = (int64_t)blockIdx.y * BM + 4 * (threadIdx.x >> 4) + tr;
+  const int64_t col = (int64_t)blockIdx.x * BN + 4 * (threadIdx.x & 15) + tc;
   uint32_t a[16], b[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
@@ -533,8 +538,8 @@ __device__ __forceinline__ void normalise2(int S0, int S1, uint32_t mn, int& X0,
 template <int MODEL, int DT>
 __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const void* A,
                                           const void* B, int64_t M, int64_t N, int64_t K,
-                                          int64_t bm, int64_t bn, int64_t s,
-                                          const int (&X)[4][4], const uint32_t (&NE)[2][4],
+                                          int64_t s, const int (&X)[4][4],
+                                          const uint32_t (&NE)[2][4],
                                           int (&Xn)[4][4], uint32_t (&NEn)[2][4]) {
   constexpr int F = Model<MODEL>::F;
   int S[4][4];
@@ -593,10 +598,10 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         // recompute the whole 4x4 tile from the previous state
-        const uint2 v0 = slow_step<MODEL, DT>(A, B, M, N, K, bm + 4 * ty + 2 * q, bn + 4 * tx + c,
-                                              s, X[2 * q][c], NE[q][c] & 0xFFFFu);
-        const uint2 v1 = slow_step<MODEL, DT>(A, B, M, N, K, bm + 4 * ty + 2 * q + 1,
-                                              bn + 4 * tx + c, s, X[2 * q + 1][c], NE[q][c] >> 16);
+        const uint2 v0 = slow_step<MODEL, DT>(A, B, M, N, K, s, 2 * q, c, X[2 * q][c],
+                                              NE[q][c] & 0xFFFFu);
+        const uint2 v1 = slow_step<MODEL, DT>(A, B, M, N, K, s, 2 * q + 1, c, X[2 * q + 1][c],
+                                              NE[q][c] >> 16);
         Xn[2 * q][c] = (int)v0.x;
         Xn[2 * q + 1][c] = (int)v1.x;
         NEn[q][c] = v0.y | v1.y << 16;
@@ -671,7 +676,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
 
   for (int64_t s = 0; s < nsteps; s += 2) {
     if (s + 1 < nsteps) begin_fill(s + 1);
-    tile_step<MODEL, DT>(&stage[s & 1], ty, tx, A, B, M, N, K, bm, bn, s, X, NE, Xn, NEn);
+    tile_step<MODEL, DT>(&stage[s & 1], ty, tx, A, B, M, N, K, s, X, NE, Xn, NEn);
     if (s + 1 < nsteps) end_fill(s + 1);
     __syncthreads();
     if (s + 1 >= nsteps) {
@@ -686,8 +691,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
       break;
     }
     if (s + 2 < nsteps) begin_fill(s + 2);
-    tile_step<MODEL, DT>(&stage[(s + 1) & 1], ty, tx, A, B, M, N, K, bm, bn, s + 1, Xn, NEn, X,
-                         NE);
+    tile_step<MODEL, DT>(&stage[(s + 1) & 1], ty, tx, A, B, M, N, K, s + 1, Xn, NEn, X, NE);
     if (s + 2 < nsteps) end_fill(s + 2);
     __syncthreads();
   }
