@@ -1,10 +1,12 @@
-"""Benchmark: bit-exact emulated MACs/s of the 4096^3 FP16 Ampere-model GEMM
-on one MI355X, with its VALU roofline and the CPU oracle timed beside it.
+"""Benchmark: bit-exact emulated MACs/s of a 4096^3 GEMM on one MI355X, with
+its VALU roofline and the CPU oracle timed beside it.
 
-One step = one emulated GEMM D = C + A.B (M = N = K = 4096, A, B FP16
-~ N(0,1), C = +0, Ampere model: 256 chained 16x16x16 steps per output, FP32
-write-back of every step, per-row xorsum fingerprint), inputs resident in
-HBM before the timed region starts.
+The default workload is the FP16 Ampere-model GEMM: one step = one emulated
+GEMM D = C + A.B (M = N = K = 4096, A, B FP16 ~ N(0,1), C = +0, Ampere
+model: 256 chained 16x16x16 steps per output, FP32 write-back of every
+step, per-row xorsum fingerprint), inputs resident in HBM before the timed
+region starts.  --workload selects the BF16 or E4M3 Hopper-model GEMM of the
+same size instead.
 
 Prints ONE JSON line.  --gpus above 1 is refused (one GPU per process and
 box; the path shards over rows of D, see the design notes).
@@ -23,22 +25,44 @@ sys.path.insert(0, ROOT)
 
 M = N = K = 4096
 MACS = M * N * K
-# Algorithmic integer work per emulated MAC of the Ampere FP16 model, in
-# 32-bit VALU issue slots (the unit of the peak below).  Per MAC: the exact
-# product, the truncating alignment shift and the signed accumulate (one
-# slot each), and the exponent add, running maximum and alignment distance
-# on exponents that fit 16 bits (half a slot each: two per 32-bit lane) =
-# 4.5.  Per output and 16-MAC step: two group-sum normalisations (about 6
-# slots each: magnitude, leading-bit search, 24-bit truncating shift, sign,
-# exponent) and the FP32 range test of the result (1) = 13/16 per MAC.
-ALG_SLOTS_PER_MAC = 4.5 + 13 / 16
+# Algorithmic integer work per emulated MAC, in 32-bit VALU issue slots (the
+# unit of the peak below).  Per MAC: the exact product, the truncating
+# alignment shift and the signed accumulate (one slot each), and the
+# exponent add, running maximum and alignment distance on exponents that
+# fit 16 bits (half a slot each: two per 32-bit lane) = 4.5.  Per output and
+# 16-MAC step: one group-sum normalisation per group (about 6 slots:
+# magnitude, leading-bit search, 24-bit truncating shift, sign, exponent;
+# Ampere has two groups, Hopper one) and the FP32 range test of the result
+# (1): 13/16 per MAC for Ampere, 7/16 for Hopper.
+ALG_SLOTS_PER_MAC = {"ampere": 4.5 + 13 / 16, "hopper": 4.5 + 7 / 16}
 # MI355X integer VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one
 # 32-bit lane operation per lane per clock.
 VALU_PEAK_OPS = 256 * 64 * 2.4e9
-# The pages' CPU simulator on the same workload: 50.8 s for 4096^3 on an
-# Apple M4 Pro (Hawkeye notes, "Experiments and results", Table 1).
-PAGES_MACS_PER_S = MACS / 50.8
-WORKLOAD = "gemm_4096x4096x4096_fp16_ampere"
+
+# name -> (model, model id, dtype name, dtype id, (input generator, seed),
+#          input description, the pages' CPU-simulator seconds for this
+#          4096x4096 MatMul on an Apple M4 Pro: Hawkeye notes, "Experiments
+#          and results", Table 1)
+WORKLOADS = {
+    "gemm_4096x4096x4096_fp16_ampere":
+        ("ampere", 0, "fp16", 0, ("gemm_normal", 3001),
+         "synthetic: A, B FP16 ~N(0,1) seed 3001, C = +0", 50.8),
+    "gemm_4096x4096x4096_bf16_hopper":
+        ("hopper", 1, "bf16", 1, ("gemm_wide_bf16", 4001),
+         "synthetic: A, B BF16 random sign, magnitude 2^U(-60,60), A rows 0 mod 16 "
+         "scaled by 2^16, C ~N(0,1) seed 4001", 48.2),
+    "gemm_4096x4096x4096_e4m3_hopper":
+        ("hopper", 1, "e4m3", 2, ("gemm_e4m3", 5001),
+         "synthetic: A, B uniform over the 254 finite E4M3 codes, C ~N(0,1) seed 5001", 40.6),
+}
+DEFAULT_WORKLOAD = "gemm_4096x4096x4096_fp16_ampere"
+# stored oracle digests of the full outputs (tests/golden/oracle_digests.json)
+DIGEST_KEY = {"gemm_4096x4096x4096_fp16_ampere": "gemm_4096_fp16_ampere",
+              "gemm_4096x4096x4096_bf16_hopper": "gemm_4096_bf16_hopper",
+              "gemm_4096x4096x4096_e4m3_hopper": "gemm_4096_e4m3_hopper"}
+# committed rocprofv3 summaries per workload: (HBM traffic, VALU counters)
+PROFILES = {"gemm_4096x4096x4096_fp16_ampere":
+            ("gemm_4096_fp16_ampere_hbm_traffic.json", "gemm_4096_fp16_ampere_valu_counters.json")}
 
 
 def parse():
@@ -46,6 +70,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU work for the oracle sample")
@@ -90,11 +115,13 @@ def main():
     import bit_exact_matrix_amd as mm
     from bit_exact_matrix_amd import inputs as I
 
+    model, model_id, dtname, dt_id, (gen, seed), data, pages_s = WORKLOADS[args.workload]
     mm.load_library()
     dev = torch.device("cuda:0")
-    A, B, C = I.gemm_normal(3001, M, N, K)
-    tA = torch.from_numpy(A.view(np.int16)).to(dev)
-    tB = torch.from_numpy(B.view(np.int16)).to(dev)
+    A, B, C = getattr(I, gen)(seed, M, N, K)
+    code_t = np.int8 if dtname == "e4m3" else np.int16
+    tA = torch.from_numpy(A.view(code_t)).to(dev)
+    tB = torch.from_numpy(B.view(code_t)).to(dev)
     tC = torch.from_numpy(C.view(np.float32)).to(dev)
     tD = torch.empty((M, N), dtype=torch.float32, device=dev)
     tX = torch.empty(M, dtype=torch.int32, device=dev)
@@ -102,8 +129,8 @@ def main():
 
     # one launch = the whole hot path (with the xorsum epilogue)
     def one():
-        rc = mm.mma_emulate_gemm_async(0, 0, tA.data_ptr(), tB.data_ptr(), tC.data_ptr(),
-                                       tD.data_ptr(), M, N, K, tX.data_ptr(),
+        rc = mm.mma_emulate_gemm_async(model_id, dt_id, tA.data_ptr(), tB.data_ptr(),
+                                       tC.data_ptr(), tD.data_ptr(), M, N, K, tX.data_ptr(),
                                        stream.cuda_stream)
         if rc:
             raise mm.MmaEmuError(rc, "mma_emulate_gemm_async")
@@ -142,20 +169,22 @@ def main():
     D = tD.cpu().numpy().view(np.uint32)
     X = tX.cpu().numpy().view(np.uint32)
     dig = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))
-    ref = dig.get("gemm_4096_fp16_ampere", {})
+    ref = dig.get(DIGEST_KEY[args.workload], {})
     bit_exact = (hashlib.sha256(D.tobytes()).hexdigest() == ref.get("D_sha256")
                  and hashlib.sha256(X.tobytes()).hexdigest() == ref.get("xorsum_sha256"))
 
     avg_launch_s = ev_total_s / args.steps
-    achieved = ALG_SLOTS_PER_MAC * MACS / avg_launch_s
+    alg = ALG_SLOTS_PER_MAC[model]
+    achieved = alg * MACS / avg_launch_s
     khash = kernel_source_hash()
-    hbm = profile_record("gemm_4096_fp16_ampere_hbm_traffic.json", khash)
-    valu = profile_record("gemm_4096_fp16_ampere_valu_counters.json", khash)
+    hbm_name, valu_name = PROFILES.get(args.workload, (None, None))
+    hbm = profile_record(hbm_name, khash) if hbm_name else None
+    valu = profile_record(valu_name, khash) if valu_name else None
     roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3),
                 "peak": round(VALU_PEAK_OPS / 1e12, 3), "unit": "TOP/s",
                 "frac": round(achieved / VALU_PEAK_OPS, 4),
                 "traffic": hbm["bytes_per_launch"] if hbm else None,
-                "alg_slots_per_mac": ALG_SLOTS_PER_MAC,
+                "alg_slots_per_mac": alg,
                 "launch_ms_mean": round(1e3 * avg_launch_s, 4),
                 "launch_ms_min": round(min(launch_ms), 4)}
     if valu:
@@ -172,12 +201,12 @@ def main():
         nth = max(1, min(args.cpu_threads, oracle.num_cpus()))
         # calibrate on a few rows, then time a sample worth ~cpu_seconds
         t = time.perf_counter()
-        oracle.gemm_rows("ampere", "fp16", A, B, C, 0, nth, nthreads=nth)
+        oracle.gemm_rows(model, dtname, A, B, C, 0, nth, nthreads=nth)
         per_row = (time.perf_counter() - t) / nth
         rows = int(max(nth, min(M, args.cpu_seconds / max(per_row, 1e-9))))
         rows = max(nth, (rows // nth) * nth)
         t = time.perf_counter()
-        Dr, Xr = oracle.gemm_rows("ampere", "fp16", A, B, C, 0, rows, nthreads=nth)
+        Dr, Xr = oracle.gemm_rows(model, dtname, A, B, C, 0, rows, nthreads=nth)
         cs = time.perf_counter() - t
         cpu = {"value": round(rows * N * K / cs, 1), "unit": "MAC/s", "cores": nth,
                "kind": "oracle", "seconds": round(cs, 2),
@@ -186,7 +215,8 @@ def main():
                                           and np.array_equal(Xr, X[:rows]))}
 
     out = {
-        "metric": "bit-exact emulated MACs/s, 4096^3 FP16 Ampere model; % of VALU peak",
+        "metric": f"bit-exact emulated MACs/s, 4096³ {dtname.upper()} "
+                  f"{model.capitalize()} model; % of VALU peak",
         "value": round(value, 1),
         "unit": "MAC/s",
         "n_gpus": 1,
@@ -195,11 +225,11 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / PAGES_MACS_PER_S, 1),
+        "vs_baseline": round(value / (MACS / pages_s), 1),
         "dtype": "int32",
-        "data": "synthetic: A, B FP16 ~N(0,1) seed 3001, C = +0",
-        "config": {"workload": WORKLOAD, "M": M, "N": N, "K": K, "model": "ampere",
-                   "input": "fp16", "accumulator": "fp32", "xorsum": "per-row",
+        "data": data,
+        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "model": model,
+                   "input": dtname, "accumulator": "fp32", "xorsum": "per-row",
                    "parallelism": "single-gpu"},
         "bit_exact_vs_oracle": bool(bit_exact),
         "wall_s_timed": round(wall, 4),

@@ -195,9 +195,11 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, uint32_t
     void* ws = workspace_alloc(gemm_fast_workspace_bytes(M, N, K), s);
     gemm_fast_launch<MODEL, DT>(A, B, C, D, X, M, N, K, ws, s);
     if (ws) {
+      // the free is ordered after the kernels; it is issued whatever the
+      // launches returned, so that a failed call does not hold the memory
       const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) return e;
       (void)hipFreeAsync(ws, s);
+      if (e != hipSuccess) return e;
     }
   } else {
     const int64_t cb = (N + 255) / 256;

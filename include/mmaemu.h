@@ -35,8 +35,16 @@
  *
  * MEMORY AND LAYOUT
  *   Every pointer is a DEVICE pointer on the current HIP device, owned by
- *   the caller; the library keeps nothing between calls and allocates no
- *   device memory.
+ *   the caller.  mma_emulate_gemm and mma_emulate_gemm_async stage the
+ *   operands through a temporary workspace of
+ *   12 KiB x (ceil(M/64) + ceil(N/64)) x K/16 bytes (384 MiB at 4096^3),
+ *   allocated and freed in stream order from a per-device memory pool that
+ *   the library creates on first use and keeps, with the memory it has
+ *   cached, until the process ends.  If that allocation fails, or the
+ *   environment variable MMAEMU_NO_WORKSPACE is set, the call stages the
+ *   operands in LDS instead (same results, slower) and allocates nothing.
+ *   mma_emulate_tiles allocates nothing.  No other state is kept between
+ *   calls.
  *   A  M x K row-major raw codes: uint16 (FP16, BF16) or uint8 (E4M3)
  *   B  K x N row-major raw codes, same type
  *   C  M x N row-major FP32 (read as bit patterns); NULL means all +0.0
