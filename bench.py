@@ -6,7 +6,9 @@ GEMM D = C + A.B (M = N = K = 4096, A, B FP16 ~ N(0,1), C = +0, Ampere
 model: 256 chained 16x16x16 steps per output, FP32 write-back of every
 step, per-row xorsum fingerprint), inputs resident in HBM before the timed
 region starts.  --workload selects the BF16 or E4M3 Hopper-model GEMM of the
-same size instead.
+same size instead.  --verify times the audit compare (mma_verify_gemm: the
+same emulation, compared bit for bit with a claimed D instead of stored)
+against a claimed D equal to the oracle's.
 
 Prints ONE JSON line.  --gpus above 1 is refused (one GPU per process and
 box; the path shards over rows of D, see the design notes).
@@ -71,6 +73,8 @@ def parse():
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD)
+    p.add_argument("--verify", action="store_true",
+                   help="time the audit compare against a claimed D instead of the GEMM")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU work for the oracle sample")
@@ -128,12 +132,33 @@ def main():
     stream = torch.cuda.current_stream()
 
     # one launch = the whole hot path (with the xorsum epilogue)
-    def one():
+    def emulate():
         rc = mm.mma_emulate_gemm_async(model_id, dt_id, tA.data_ptr(), tB.data_ptr(),
                                        tC.data_ptr(), tD.data_ptr(), M, N, K, tX.data_ptr(),
                                        stream.cuda_stream)
         if rc:
             raise mm.MmaEmuError(rc, "mma_emulate_gemm_async")
+
+    dig = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))
+    ref = dig.get(DIGEST_KEY[args.workload], {})
+    one = emulate
+    if args.verify:
+        # the claimed D: the emulated one, whose digest must be the oracle's
+        emulate()
+        torch.cuda.synchronize()
+        claimed = tD.clone()
+        claimed_ok = (hashlib.sha256(claimed.cpu().numpy().tobytes()).hexdigest()
+                      == ref.get("D_sha256"))
+        report = torch.empty(2, dtype=torch.int64, device=dev)
+
+        def verify():
+            rc = mm.mma_verify_gemm_async(model_id, dt_id, tA.data_ptr(), tB.data_ptr(),
+                                          tC.data_ptr(), claimed.data_ptr(), M, N, K,
+                                          report.data_ptr(), tX.data_ptr(),
+                                          stream.cuda_stream)
+            if rc:
+                raise mm.MmaEmuError(rc, "mma_verify_gemm_async")
+        one = verify
 
     for _ in range(args.warmup):
         one()
@@ -168,16 +193,29 @@ def main():
     # parity of the timed output against the oracle's full-output digest
     D = tD.cpu().numpy().view(np.uint32)
     X = tX.cpu().numpy().view(np.uint32)
-    dig = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))
-    ref = dig.get(DIGEST_KEY[args.workload], {})
-    bit_exact = (hashlib.sha256(D.tobytes()).hexdigest() == ref.get("D_sha256")
-                 and hashlib.sha256(X.tobytes()).hexdigest() == ref.get("xorsum_sha256"))
+    if args.verify:
+        # the timed reports must be clean; then three planted flips must be
+        # found exactly (count, first index, row words)
+        clean = mm.mismatches(report) == (0, None) and not X.any()
+        flips = [(7, 123, 0x1), (2049, 4000, 0x80000000), (4095, 0, 0x00400000)]
+        for r, c, m in flips:
+            sm = m - (1 << 32) if m >= 1 << 31 else m   # the mask as an int32 value
+            claimed[r, c] = (claimed[r, c].view(torch.int32) ^ sm).view(torch.float32)
+        verify()
+        X = tX.cpu().numpy().view(np.uint32)
+        rows_ok = all(X[r] == m for r, c, m in flips) and np.count_nonzero(X) == len(flips)
+        bit_exact = bool(claimed_ok and clean and rows_ok
+                         and mm.mismatches(report) == (3, 7 * N + 123))
+    else:
+        bit_exact = (hashlib.sha256(D.tobytes()).hexdigest() == ref.get("D_sha256")
+                     and hashlib.sha256(X.tobytes()).hexdigest() == ref.get("xorsum_sha256"))
 
     avg_launch_s = ev_total_s / args.steps
     alg = ALG_SLOTS_PER_MAC[model]
     achieved = alg * MACS / avg_launch_s
     khash = kernel_source_hash()
-    hbm_name, valu_name = PROFILES.get(args.workload, (None, None))
+    hbm_name, valu_name = (None, None) if args.verify else PROFILES.get(args.workload,
+                                                                        (None, None))
     hbm = profile_record(hbm_name, khash) if hbm_name else None
     valu = profile_record(valu_name, khash) if valu_name else None
     roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3),
@@ -212,11 +250,11 @@ def main():
                "kind": "oracle", "seconds": round(cs, 2),
                "sample": f"rows 0..{rows - 1} of D ({rows}x{N}x{K} MACs) of the same GEMM",
                "sample_matches_gpu": bool(np.array_equal(Dr, D[:rows])
-                                          and np.array_equal(Xr, X[:rows]))}
+                                          and (args.verify or np.array_equal(Xr, X[:rows])))}
 
     out = {
-        "metric": f"bit-exact emulated MACs/s, 4096³ {dtname.upper()} "
-                  f"{model.capitalize()} model; % of VALU peak",
+        "metric": (f"bit-exact {'audit-compare' if args.verify else 'emulated'} MACs/s, "
+                   f"4096³ {dtname.upper()} {model.capitalize()} model; % of VALU peak"),
         "value": round(value, 1),
         "unit": "MAC/s",
         "n_gpus": 1,
@@ -228,7 +266,8 @@ def main():
         "vs_baseline": round(value / (MACS / pages_s), 1),
         "dtype": "int32",
         "data": data,
-        "config": {"workload": args.workload, "M": M, "N": N, "K": K, "model": model,
+        "config": {"workload": args.workload + ("_verify" if args.verify else ""),
+                   "M": M, "N": N, "K": K, "model": model,
                    "input": dtname, "accumulator": "fp32", "xorsum": "per-row",
                    "parallelism": "single-gpu"},
         "bit_exact_vs_oracle": bool(bit_exact),

@@ -7,10 +7,11 @@ CPU fallback: if the library is missing or no GPU is present, the calls
 raise.
 
 The raw C entry points are available under their own names
-(``mma_emulate_gemm``, ``mma_emulate_gemm_async``, ``mma_emulate_tiles``,
-``mma_emulate_strerror``, ``mma_emulate_spec_version``) and take integers
-(device pointers) exactly as the C functions do; ``gemm`` and ``tiles`` wrap
-them for torch tensors.
+(``mma_emulate_gemm``, ``mma_emulate_gemm_async``, ``mma_verify_gemm``,
+``mma_verify_gemm_async``, ``mma_emulate_tiles``, ``mma_emulate_strerror``,
+``mma_emulate_spec_version``) and take integers (device pointers) exactly as
+the C functions do; ``gemm``, ``verify`` and ``tiles`` wrap them for torch
+tensors.
 """
 from __future__ import annotations
 
@@ -24,8 +25,9 @@ AMPERE, HOPPER = 0, 1
 FP16, BF16, FP8_E4M3 = 0, 1, 2
 MODELS = {"ampere": AMPERE, "hopper": HOPPER}
 DTYPES = {"fp16": FP16, "bf16": BF16, "e4m3": FP8_E4M3, "fp8_e4m3": FP8_E4M3}
-EXPORTED = ("mma_emulate_gemm", "mma_emulate_gemm_async", "mma_emulate_tiles",
-            "mma_emulate_strerror", "mma_emulate_spec_version")
+EXPORTED = ("mma_emulate_gemm", "mma_emulate_gemm_async", "mma_verify_gemm",
+            "mma_verify_gemm_async", "mma_emulate_tiles", "mma_emulate_strerror",
+            "mma_emulate_spec_version")
 
 
 class MmaEmuError(RuntimeError):
@@ -47,11 +49,15 @@ def load_library(path: str = LIB_PATH):
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.mma_emulate_gemm.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp]
         lib.mma_emulate_gemm_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp]
+        lib.mma_verify_gemm.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp]
+        lib.mma_verify_gemm_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp,
+                                              vp]
         lib.mma_emulate_tiles.argtypes = [i32, i32, vp, vp, vp, vp, i64, vp, vp]
         lib.mma_emulate_strerror.argtypes = [i32]
         lib.mma_emulate_strerror.restype = ctypes.c_char_p
         lib.mma_emulate_spec_version.argtypes = []
-        for f in (lib.mma_emulate_gemm, lib.mma_emulate_gemm_async, lib.mma_emulate_tiles,
+        for f in (lib.mma_emulate_gemm, lib.mma_emulate_gemm_async, lib.mma_verify_gemm,
+                  lib.mma_verify_gemm_async, lib.mma_emulate_tiles,
                   lib.mma_emulate_spec_version):
             f.restype = i32
         _lib = lib
@@ -66,6 +72,17 @@ def mma_emulate_gemm(model, dtype, A, B, C, D, M, N, K, xorsum_out):
 def mma_emulate_gemm_async(model, dtype, A, B, C, D, M, N, K, xorsum_out, hip_stream):
     return load_library().mma_emulate_gemm_async(model, dtype, A, B, C, D, M, N, K,
                                                  xorsum_out, hip_stream)
+
+
+def mma_verify_gemm(model, dtype, A, B, C, D_claimed, M, N, K, report, row_diff_out):
+    return load_library().mma_verify_gemm(model, dtype, A, B, C, D_claimed, M, N, K, report,
+                                          row_diff_out)
+
+
+def mma_verify_gemm_async(model, dtype, A, B, C, D_claimed, M, N, K, report, row_diff_out,
+                          hip_stream):
+    return load_library().mma_verify_gemm_async(model, dtype, A, B, C, D_claimed, M, N, K,
+                                                report, row_diff_out, hip_stream)
 
 
 def mma_emulate_tiles(model, dtype, A, B, C, D, ntiles, xorsum_out, hip_stream):
@@ -99,6 +116,11 @@ def _dev_ptr(t, what, nbytes_elem=None):
     return t.data_ptr()
 
 
+def _check_shape(t, shape, what):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 def _stream_handle(stream):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
@@ -120,6 +142,8 @@ def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
     K2, N = B.shape
     if K != K2:
         raise ValueError("inner dimensions differ")
+    _check_shape(C, (M, N), "C")
+    _check_shape(D, (M, N), "D")
     if D is None:
         D = torch.empty((M, N), dtype=torch.float32, device=A.device)
     X = torch.empty(M, dtype=torch.int32, device=A.device) if xorsum else None
@@ -131,6 +155,42 @@ def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
     return D, X
 
 
+def verify(model, dtype, A, B, C, D_claimed, row_diff=False, stream=None):
+    """Audit compare: emulate D = C + A.B and compare it bit for bit with
+    D_claimed (M x N float32, bit patterns) without storing it.
+
+    Returns (report, row_diff) as device tensors, enqueued on the stream:
+    report int64[2] = (number of differing elements, smallest differing
+    row-major index or -1 when none; the C ABI's UINT64_MAX read as int64),
+    row_diff int32 of M words (XOR over each row of emulated ^ claimed) or
+    None.  ``mismatches(report)`` turns the report into Python ints.
+    """
+    import torch
+    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    esz = 1 if d == FP8_E4M3 else 2
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    _check_shape(C, (M, N), "C")
+    _check_shape(D_claimed, (M, N), "D_claimed")
+    report = torch.empty(2, dtype=torch.int64, device=A.device)
+    X = torch.empty(M, dtype=torch.int32, device=A.device) if row_diff else None
+    rc = mma_verify_gemm_async(m, d, _dev_ptr(A, "A", esz), _dev_ptr(B, "B", esz),
+                               _dev_ptr(C, "C", 4), _dev_ptr(D_claimed, "D_claimed", 4),
+                               M, N, K, _dev_ptr(report, "report"), _dev_ptr(X, "row_diff"),
+                               _stream_handle(stream))
+    if rc != 0:
+        raise MmaEmuError(rc, "mma_verify_gemm_async")
+    return report, X
+
+
+def mismatches(report):
+    """(count, first index or None) from a verify() report tensor."""
+    count, first = (int(v) for v in report.cpu().tolist())
+    return count, (None if first == -1 else first)
+
+
 def tiles(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
     """ntiles independent 16x16x16 MMAs: A, B [n,16,16] codes, C [n,16,16] f32."""
     import torch
@@ -139,6 +199,8 @@ def tiles(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
     n = A.shape[0]
     if tuple(A.shape) != (n, 16, 16) or tuple(B.shape) != (n, 16, 16):
         raise ValueError("A and B must be [ntiles, 16, 16]")
+    _check_shape(C, (n, 16, 16), "C")
+    _check_shape(D, (n, 16, 16), "D")
     if D is None:
         D = torch.empty((n, 16, 16), dtype=torch.float32, device=A.device)
     X = torch.empty(n, dtype=torch.int32, device=A.device) if xorsum else None

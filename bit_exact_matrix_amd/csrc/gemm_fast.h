@@ -624,9 +624,9 @@ constexpr int kWavesPerSimd = DMA ? 3 : 2;
 // being copied back every step.
 template <int MODEL, int DT, bool DMA>
 __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_kernel(
-    const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, uint32_t* D,
-    uint32_t* __restrict__ xorsum, int64_t M, int64_t N, int64_t K,
-    const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b) {
+    const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
+    int64_t M, int64_t N, int64_t K, const uint32_t* __restrict__ ws_a,
+    const uint32_t* __restrict__ ws_b) {
   __shared__ Stage stage[2];
   const int t = threadIdx.x;
   const int ty = t >> 4, tx = t & 15;
@@ -697,6 +697,8 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
   }
 
   uint32_t rowx[4] = {0, 0, 0, 0};
+  uint32_t nbad = 0;
+  unsigned long long first = ~0ull;
 #pragma unroll
   for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -704,10 +706,22 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
       const int64_t row = bm + 4 * ty + r, col = bn + 4 * tx + c;
       const uint32_t d = state_to_bits<MODEL>(X[r][c], half16(NE[r >> 1][c], r & 1));
       if (row < M && col < N) {
-        D[row * N + col] = d;
-        rowx[r] ^= d;
+        const int64_t idx = row * N + col;
+        if (out.claimed) {
+          const uint32_t x = d ^ out.claimed[idx];
+          rowx[r] ^= x;
+          if (x) {
+            ++nbad;
+            first = (unsigned long long)idx < first ? (unsigned long long)idx : first;
+          }
+        } else {
+          out.D[idx] = d;
+          rowx[r] ^= d;
+        }
       }
     }
+  if (out.claimed) report_mismatches(out.report, nbad, first);
+  uint32_t* const xorsum = out.xorsum;
   if (xorsum) {
     // XOR across the 16 lanes that share these rows (one 16-lane row of the wave)
 #pragma unroll
@@ -736,9 +750,8 @@ inline int64_t gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 
 // ws: NULL for the in-kernel image build, else gemm_fast_workspace_bytes() bytes.
 template <int MODEL, int DT>
-inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, uint32_t* D,
-                             uint32_t* X, int64_t M, int64_t N, int64_t K, void* ws,
-                             hipStream_t s) {
+inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, const Sink& out,
+                             int64_t M, int64_t N, int64_t K, void* ws, hipStream_t s) {
   const int64_t mb = (M + fastk::BM - 1) / fastk::BM, nb = (N + fastk::BN - 1) / fastk::BN;
   const int64_t nsteps = K / 16;
   const dim3 grid((unsigned)nb, (unsigned)mb);
@@ -750,10 +763,10 @@ inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, ui
     fastk::unpack_kernel<MODEL, DT, true>
         <<<dim3((unsigned)nsteps, (unsigned)nb), dim3(64), 0, s>>>(B, N, K, N, nsteps, ws_b);
     fastk::gemm_fast_kernel<MODEL, DT, true>
-        <<<grid, dim3(fastk::NT), 0, s>>>(A, B, C, D, X, M, N, K, ws_a, ws_b);
+        <<<grid, dim3(fastk::NT), 0, s>>>(A, B, C, out, M, N, K, ws_a, ws_b);
   } else {
     fastk::gemm_fast_kernel<MODEL, DT, false>
-        <<<grid, dim3(fastk::NT), 0, s>>>(A, B, C, D, X, M, N, K, nullptr, nullptr);
+        <<<grid, dim3(fastk::NT), 0, s>>>(A, B, C, out, M, N, K, nullptr, nullptr);
   }
 }
 

@@ -59,12 +59,14 @@ __global__ __launch_bounds__(256) void tiles_kernel(const void* __restrict__ A,
 // Kept as the simple, fully general path (any shape, any input bits).
 template <int MODEL, int DT>
 __global__ __launch_bounds__(256) void gemm_reference_kernel(
-    const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C,
-    uint32_t* D, uint32_t* __restrict__ xorsum, int64_t M, int64_t N, int64_t K) {
+    const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
+    int64_t M, int64_t N, int64_t K) {
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool live = col < N;
+  uint32_t nbad = 0;
+  unsigned long long first = ~0ull;
   for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
-    uint32_t c = 0;
+    uint32_t c = 0, x = 0;
     if (live) {
       c = C ? C[row * N + col] : 0u;
       for (int64_t t = 0; t < K / 16; ++t) {
@@ -76,18 +78,37 @@ __global__ __launch_bounds__(256) void gemm_reference_kernel(
         }
         c = step_generic<MODEL, DT>(c, a, b);
       }
-      D[row * N + col] = c;
+      const int64_t idx = row * N + col;
+      if (out.claimed) {
+        x = c ^ out.claimed[idx];
+        if (x) {
+          ++nbad;
+          first = (unsigned long long)idx < first ? (unsigned long long)idx : first;
+        }
+      } else {
+        out.D[idx] = c;
+        x = c;
+      }
     }
-    if (xorsum) {
-      const uint32_t w = wave_xor(live ? c : 0u);
-      if ((threadIdx.x & 63) == 0 && w) atomicXor(&xorsum[row], w);
+    if (out.xorsum) {
+      const uint32_t w = wave_xor(x);
+      if ((threadIdx.x & 63) == 0 && w) atomicXor(&out.xorsum[row], w);
     }
   }
+  if (out.claimed) report_mismatches(out.report, nbad, first);
 }
 
 __global__ void fill_zero_kernel(uint32_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = 0u;
+}
+
+// report = {0 mismatches, no mismatching index}
+__global__ void init_report_kernel(unsigned long long* report) {
+  if (threadIdx.x == 0) {
+    report[0] = 0ull;
+    report[1] = ~0ull;
+  }
 }
 
 // ------------------------------------------------------------- plumbing
@@ -133,6 +154,21 @@ int check_alias(const void* A, int64_t abytes, const void* B, int64_t bbytes,
       overlap(rx, rc) || overlap(rx, rd))
     return MMAEMU_ERR_ALIAS;
   if (C && C != D && overlap(rc, rd)) return MMAEMU_ERR_ALIAS;
+  return MMAEMU_OK;
+}
+
+// Verify mode: A, B, C and the claimed D are read-only (they may overlap
+// one another); the report and the row words are written and may overlap
+// nothing.
+int check_alias_verify(const void* A, int64_t abytes, const void* B, int64_t bbytes,
+                       const void* C, const void* Dc, int64_t cdbytes, const void* R,
+                       const void* X, int64_t xbytes) {
+  const Range in[4] = {range_of(A, abytes), range_of(B, bbytes), range_of(C, cdbytes),
+                       range_of(Dc, cdbytes)};
+  const Range rr = range_of(R, 16), rx = range_of(X, xbytes);
+  if (overlap(rr, rx)) return MMAEMU_ERR_ALIAS;
+  for (const Range& r : in)
+    if (overlap(rr, r) || overlap(rx, r)) return MMAEMU_ERR_ALIAS;
   return MMAEMU_OK;
 }
 
@@ -185,15 +221,17 @@ void* workspace_alloc(int64_t bytes, hipStream_t s) {
 }
 
 template <int MODEL, int DT>
-hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, uint32_t* D,
-                       uint32_t* X, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  if (X) {
+hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Sink& out,
+                       int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  if (out.xorsum && M > 0) {
     const int64_t blocks = (M + 255) / 256;
-    fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(X, M);
+    fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(out.xorsum, M);
   }
+  if (out.report) init_report_kernel<<<dim3(1), dim3(64), 0, s>>>(out.report);
+  if (M == 0 || N == 0) return hipGetLastError();
   if (gemm_fast_supported(M, N, K)) {
     void* ws = workspace_alloc(gemm_fast_workspace_bytes(M, N, K), s);
-    gemm_fast_launch<MODEL, DT>(A, B, C, D, X, M, N, K, ws, s);
+    gemm_fast_launch<MODEL, DT>(A, B, C, out, M, N, K, ws, s);
     if (ws) {
       // the free is ordered after the kernels; it is issued whatever the
       // launches returned, so that a failed call does not hold the memory
@@ -205,7 +243,7 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, uint32_t
     const int64_t cb = (N + 255) / 256;
     const int64_t rows = M < 32768 ? M : 32768;
     gemm_reference_kernel<MODEL, DT>
-        <<<dim3((unsigned)cb, (unsigned)rows), dim3(256), 0, s>>>(A, B, C, D, X, M, N, K);
+        <<<dim3((unsigned)cb, (unsigned)rows), dim3(256), 0, s>>>(A, B, C, out, M, N, K);
   }
   return hipGetLastError();
 }
@@ -226,25 +264,63 @@ hipError_t launch_tiles(const void* A, const void* B, const uint32_t* C, uint32_
               : ((dtype) == MMAEMU_DTYPE_BF16 ? FN<kHopper, kBF16>(__VA_ARGS__) \
                                               : FN<kHopper, kE4M3>(__VA_ARGS__))))
 
+// Byte sizes of a GEMM's operands; false if the shape is invalid.
+struct GemmBytes {
+  int64_t a, b, cd;
+};
+
+int check_gemm_shape(int dtype, int64_t M, int64_t N, int64_t K, GemmBytes* g) {
+  if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return MMAEMU_ERR_SHAPE;
+  const int64_t esz = dtype == MMAEMU_DTYPE_FP8_E4M3 ? 1 : 2;
+  int64_t mk, kn, mn;
+  if (!mul_ok(M, K, &mk) || !mul_ok(K, N, &kn) || !mul_ok(M, N, &mn) ||
+      !mul_ok(mk, esz, &g->a) || !mul_ok(kn, esz, &g->b) || !mul_ok(mn, 4, &g->cd))
+    return MMAEMU_ERR_SHAPE;
+  if (N > (int64_t)INT32_MAX || M > (int64_t)INT32_MAX * 256) return MMAEMU_ERR_SHAPE;
+  return MMAEMU_OK;
+}
+
 int gemm_impl(int model, int dtype, const void* A, const void* B, const float* C,
               float* D, int64_t M, int64_t N, int64_t K, uint32_t* xorsum,
               hipStream_t s) {
   int rc = check_model_dtype(model, dtype);
   if (rc) return rc;
-  if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return MMAEMU_ERR_SHAPE;
-  const int64_t esz = dtype == MMAEMU_DTYPE_FP8_E4M3 ? 1 : 2;
-  int64_t mk, kn, mn, ab, bb, cb;
-  if (!mul_ok(M, K, &mk) || !mul_ok(K, N, &kn) || !mul_ok(M, N, &mn) ||
-      !mul_ok(mk, esz, &ab) || !mul_ok(kn, esz, &bb) || !mul_ok(mn, 4, &cb))
-    return MMAEMU_ERR_SHAPE;
-  if (N > (int64_t)INT32_MAX || M > (int64_t)INT32_MAX * 256) return MMAEMU_ERR_SHAPE;
-  if (mn == 0) return MMAEMU_OK;
-  if (!D || (K > 0 && (!A || !B))) return MMAEMU_ERR_NULL;
-  rc = check_alias(A, K ? ab : 0, B, K ? bb : 0, C, D, cb, xorsum, xorsum ? M * 4 : 0);
+  GemmBytes g;
+  rc = check_gemm_shape(dtype, M, N, K, &g);
   if (rc) return rc;
-  const hipError_t e = MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C,
-                                       (uint32_t*)D, xorsum, M, N, K, s);
+  // an empty D: nothing to compute; the xorsum words of its M empty rows
+  // are still written (as zeros)
+  if (g.cd == 0 && !(xorsum && M > 0)) return MMAEMU_OK;
+  if (g.cd > 0 && (!D || (K > 0 && (!A || !B)))) return MMAEMU_ERR_NULL;
+  rc = check_alias(g.cd && K ? A : nullptr, g.a, g.cd && K ? B : nullptr, g.b,
+                   g.cd ? C : nullptr, g.cd ? D : nullptr, g.cd, xorsum, xorsum ? M * 4 : 0);
+  if (rc) return rc;
+  const Sink out{(uint32_t*)D, xorsum, nullptr, nullptr};
+  const hipError_t e =
+      MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C, out, M, N, K, s);
   if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm launch");
+  return MMAEMU_OK;
+}
+
+int verify_impl(int model, int dtype, const void* A, const void* B, const float* C,
+                const float* D_claimed, int64_t M, int64_t N, int64_t K, uint64_t* report,
+                uint32_t* row_diff, hipStream_t s) {
+  int rc = check_model_dtype(model, dtype);
+  if (rc) return rc;
+  GemmBytes g;
+  rc = check_gemm_shape(dtype, M, N, K, &g);
+  if (rc) return rc;
+  if (!report) return MMAEMU_ERR_NULL;
+  if (g.cd > 0 && (!D_claimed || (K > 0 && (!A || !B)))) return MMAEMU_ERR_NULL;
+  const bool any = g.cd > 0;
+  rc = check_alias_verify(any && K ? A : nullptr, g.a, any && K ? B : nullptr, g.b,
+                          any ? C : nullptr, any ? D_claimed : nullptr, g.cd, report,
+                          row_diff, row_diff ? M * 4 : 0);
+  if (rc) return rc;
+  const Sink out{nullptr, row_diff, (const uint32_t*)D_claimed, (unsigned long long*)report};
+  const hipError_t e =
+      MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C, out, M, N, K, s);
+  if (e != hipSuccess) return hip_fail(e, "mma_verify_gemm launch");
   return MMAEMU_OK;
 }
 
@@ -264,6 +340,25 @@ int mma_emulate_gemm(int model, int dtype, const void* A, const void* B, const f
   if (rc) return rc;
   const hipError_t e = hipStreamSynchronize(nullptr);
   if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm synchronize");
+  return MMAEMU_OK;
+}
+
+int mma_verify_gemm_async(int model, int dtype, const void* A, const void* B,
+                          const float* C, const float* D_claimed, int64_t M, int64_t N,
+                          int64_t K, uint64_t* report, uint32_t* row_diff_out,
+                          void* hip_stream) {
+  return verify_impl(model, dtype, A, B, C, D_claimed, M, N, K, report, row_diff_out,
+                     (hipStream_t)hip_stream);
+}
+
+int mma_verify_gemm(int model, int dtype, const void* A, const void* B, const float* C,
+                    const float* D_claimed, int64_t M, int64_t N, int64_t K, uint64_t* report,
+                    uint32_t* row_diff_out) {
+  const int rc =
+      verify_impl(model, dtype, A, B, C, D_claimed, M, N, K, report, row_diff_out, nullptr);
+  if (rc) return rc;
+  const hipError_t e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) return hip_fail(e, "mma_verify_gemm synchronize");
   return MMAEMU_OK;
 }
 

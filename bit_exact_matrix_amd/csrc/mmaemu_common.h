@@ -257,4 +257,37 @@ __device__ __forceinline__ uint32_t wave_xor(uint32_t v) {
   return v;
 }
 
+// Where a GEMM's results go.
+//   Store mode (claimed == NULL): D receives the result; xorsum, if not
+//   NULL, the XOR of each row of D.
+//   Verify mode (claimed != NULL): nothing is stored.  Each result is
+//   compared bit for bit with claimed; report[0] counts the mismatching
+//   elements and report[1] keeps the smallest mismatching row-major index
+//   (both set up by the host before the kernel: 0 and all ones); xorsum, if
+//   not NULL, receives the XOR over each row of (result ^ claimed).
+struct Sink {
+  uint32_t* D;
+  uint32_t* xorsum;
+  const uint32_t* claimed;
+  unsigned long long* report;
+};
+
+// Folds one lane's mismatch count and smallest mismatching index into the
+// report, once per wavefront.  Every lane of the wavefront must call it.
+__device__ __forceinline__ void report_mismatches(unsigned long long* report, uint32_t n,
+                                                  unsigned long long first) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    n += __shfl_xor(n, off, 64);
+    const uint32_t lo = __shfl_xor((uint32_t)first, off, 64);
+    const uint32_t hi = __shfl_xor((uint32_t)(first >> 32), off, 64);
+    const unsigned long long o = ((unsigned long long)hi << 32) | lo;
+    first = o < first ? o : first;
+  }
+  if ((threadIdx.x & 63) == 0 && n) {
+    atomicAdd(&report[0], (unsigned long long)n);
+    atomicMin(&report[1], first);
+  }
+}
+
 }  // namespace mmaemu

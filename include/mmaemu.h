@@ -49,7 +49,8 @@
  *   B  K x N row-major raw codes, same type
  *   C  M x N row-major FP32 (read as bit patterns); NULL means all +0.0
  *   D  M x N row-major FP32 bit patterns; D == C (exactly) is allowed
- *   xorsum_out  NULL, or M uint32 words (overwritten, not accumulated)
+ *   xorsum_out  NULL, or M uint32 words (overwritten, not accumulated; the
+ *              words of empty rows, N = 0, are written as 0)
  *   Shapes: M >= 0, N >= 0, K >= 0 with K a multiple of 16.  Empty
  *   operands are allowed (K = 0 gives D = C).
  *
@@ -102,6 +103,40 @@ int mma_emulate_gemm(int model, int dtype, const void *A, const void *B,
 int mma_emulate_gemm_async(int model, int dtype, const void *A, const void *B,
                            const float *C, float *D, int64_t M, int64_t N,
                            int64_t K, uint32_t *xorsum_out, void *hip_stream);
+
+/* Audit compare: the auditor's side of the Hawkeye workflow (Hawkeye notes,
+ * "Problem and motivation" and "Relation to the verifiable-ML workflow": an
+ * auditor who knows only which GPU architecture ran a MatMul recomputes it
+ * offline with the characterised arithmetic and checks the provider's
+ * published intermediate or final outputs against it; any bit that differs
+ * is then wrong execution, not hardware non-determinism).
+ * Emulates D = C + A.B exactly as mma_emulate_gemm does
+ * and compares every element bit for bit with D_claimed (M x N FP32, read
+ * as bit patterns) instead of storing it.  Results, written on the stream:
+ *   report        2 uint64 words (device memory, required):
+ *                   report[0] = number of elements whose bits differ,
+ *                   report[1] = row-major index i*N + j of the first
+ *                               (smallest-index) differing element, or
+ *                               UINT64_MAX when none differs;
+ *   row_diff_out  NULL, or M uint32 words (overwritten): word i is the XOR
+ *                 over j of (emulated ^ claimed) bits of row i.  A non-zero
+ *                 word proves that row differs; differences can cancel in
+ *                 the XOR, so a zero word proves nothing (report[0] is
+ *                 exact).
+ * A, B, C and D_claimed are read-only and may overlap one another; report
+ * and row_diff_out may overlap nothing.  Shapes, NULL C and errors as for
+ * mma_emulate_gemm; D_claimed may be NULL only when M*N == 0.  Enqueued on
+ * hip_stream; returns after enqueue. */
+int mma_verify_gemm_async(int model, int dtype, const void *A, const void *B,
+                          const float *C, const float *D_claimed, int64_t M,
+                          int64_t N, int64_t K, uint64_t *report,
+                          uint32_t *row_diff_out, void *hip_stream);
+
+/* Same contract, blocking: enqueued on the null stream of the current
+ * device, which is then synchronised. */
+int mma_verify_gemm(int model, int dtype, const void *A, const void *B,
+                    const float *C, const float *D_claimed, int64_t M, int64_t N,
+                    int64_t K, uint64_t *report, uint32_t *row_diff_out);
 
 /* ntiles independent 16x16x16 MMA steps (the unit the Hawkeye study audits,
  * "Key observation 1"): A, B are [ntiles][16][16] row-major codes, C, D are

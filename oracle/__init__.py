@@ -118,6 +118,30 @@ def gemm(model, dtype, A, B, C=None, nthreads=0, xorsum=True, lib=None):
     return D, x
 
 
+def compare(D, D_claimed):
+    """Bitwise comparison of an emulated D with a claimed one (both M x N
+    bit patterns): (number of differing elements, smallest differing
+    row-major index or None, per-row XOR of D ^ D_claimed as uint32[M])."""
+    D = _bits32(D)
+    claimed = _bits32(D_claimed)
+    assert claimed.shape == D.shape
+    diff = D ^ claimed
+    bad = np.flatnonzero(diff)
+    rows = np.zeros(D.shape[0], np.uint32)
+    for j in range(D.shape[1]):
+        rows ^= diff[:, j]
+    return int(bad.size), (int(bad[0]) if bad.size else None), rows
+
+
+def verify(model, dtype, A, B, C, D_claimed, nthreads=0, lib=None):
+    """Audit compare, as the auditor of the Hawkeye notes does it ("Problem
+    and motivation", "Relation to the verifiable-ML workflow"): recompute
+    D = C + A.B with the characterised arithmetic and compare the provider's
+    claimed D with it bit for bit.  Returns what ``compare`` returns."""
+    D, _ = gemm(model, dtype, A, B, C, nthreads=nthreads, xorsum=False, lib=lib)
+    return compare(D, D_claimed)
+
+
 def gemm_rows(model, dtype, A, B, C, row_begin, row_end, nthreads=0, lib=None):
     """Rows [row_begin, row_end) of D and their xorsums."""
     lib = lib or _load()

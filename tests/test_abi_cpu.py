@@ -58,9 +58,10 @@ def test_gemm_argument_errors(args, code):
 
 
 def test_gemm_empty_is_a_no_op():
-    # M = 0 or N = 0: nothing to compute, nothing enqueued
+    # an empty D with no xorsum words to write: nothing is enqueued (with
+    # M > 0 rows and N = 0 the M xorsum words are written, on the GPU)
     assert mm.mma_emulate_gemm_async(0, 0, A, B, C, D, 0, 32, 32, X, None) == 0
-    assert mm.mma_emulate_gemm_async(1, 2, A, B, C, D, 32, 0, 32, X, None) == 0
+    assert mm.mma_emulate_gemm_async(1, 2, A, B, C, D, 32, 0, 32, 0, None) == 0
 
 
 @pytest.mark.parametrize("args,code", [
@@ -81,3 +82,23 @@ def test_tiles_empty_is_a_no_op():
 def test_in_place_c_equals_d_passes_validation_only():
     # D == C is allowed; with M = 0 nothing runs, so this checks the alias rule alone
     assert mm.mma_emulate_gemm_async(0, 0, A, B, C, C, 0, 16, 16, X, None) == 0
+
+
+R = 0x60000000  # fake report address
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 0, A, B, C, D, 32, 32, 32, R, X), -1),        # unknown model
+    ((0, 2, A, B, C, D, 32, 32, 32, R, X), -3),        # E4M3 with Ampere
+    ((0, 0, A, B, C, D, 32, 32, 24, R, X), -4),        # K not a multiple of 16
+    ((0, 0, A, B, C, D, 32, 32, 32, 0, X), -5),        # NULL report
+    ((0, 0, A, B, C, 0, 32, 32, 32, R, X), -5),        # NULL claimed D
+    ((0, 0, A, 0, C, D, 32, 32, 32, R, X), -5),        # NULL B with K > 0
+    ((0, 0, A, B, C, D, 32, 32, 32, D + 8, X), -6),    # report inside the claimed D
+    ((0, 0, A, B, C, D, 32, 32, 32, R, A + 4), -6),    # row words inside A
+    ((0, 0, A, B, C, D, 32, 32, 32, R, R + 8), -6),    # row words overlap the report
+    ((0, 0, A, B, C, D, 32, 32, 32, C + 64, X), -6),   # report inside C
+])
+def test_verify_argument_errors(args, code):
+    assert mm.mma_verify_gemm_async(*args, None) == code
+    assert mm.mma_verify_gemm(*args) == code
