@@ -21,9 +21,9 @@ import os
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmmaemu.so")
 
-AMPERE, HOPPER = 0, 1
+AMPERE, HOPPER, LOVELACE = 0, 1, 2
 FP16, BF16, FP8_E4M3 = 0, 1, 2
-MODELS = {"ampere": AMPERE, "hopper": HOPPER}
+MODELS = {"ampere": AMPERE, "hopper": HOPPER, "lovelace": LOVELACE}
 DTYPES = {"fp16": FP16, "bf16": BF16, "e4m3": FP8_E4M3, "fp8_e4m3": FP8_E4M3}
 EXPORTED = ("mma_emulate_gemm", "mma_emulate_gemm_async", "mma_verify_gemm",
             "mma_verify_gemm_async", "mma_emulate_tiles", "mma_emulate_strerror",

@@ -696,6 +696,12 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
     __syncthreads();
   }
 
+  // the epilogue's addresses are recomputed from opaque copies of the lane
+  // indices, so that the compiler does not keep the prologue's 64-bit
+  // addresses live (spilled) across the K loop
+  int ety = ty, etx = tx;
+  asm volatile("" : "+v"(ety), "+v"(etx));
+  const int64_t ebm = (int64_t)blockIdx.y * BM, ebn = (int64_t)blockIdx.x * BN;
   uint32_t rowx[4] = {0, 0, 0, 0};
   uint32_t nbad = 0;
   unsigned long long first = ~0ull;
@@ -703,7 +709,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      const int64_t row = bm + 4 * ty + r, col = bn + 4 * tx + c;
+      const int64_t row = ebm + 4 * ety + r, col = ebn + 4 * etx + c;
       const uint32_t d = state_to_bits<MODEL>(X[r][c], half16(NE[r >> 1][c], r & 1));
       if (row < M && col < N) {
         const int64_t idx = row * N + col;
@@ -729,8 +735,8 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
       uint32_t v = rowx[r];
 #pragma unroll
       for (int off = 8; off >= 1; off >>= 1) v ^= __shfl_xor(v, off, 16);
-      const int64_t row = bm + 4 * ty + r;
-      if (tx == 0 && row < M && v) atomicXor(&xorsum[row], v);
+      const int64_t row = ebm + 4 * ety + r;
+      if (etx == 0 && row < M && v) atomicXor(&xorsum[row], v);
     }
   }
 }

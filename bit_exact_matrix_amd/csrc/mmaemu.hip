@@ -121,7 +121,9 @@ int hip_fail(hipError_t e, const char* where) {
 }
 
 int check_model_dtype(int model, int dtype) {
-  if (model != MMAEMU_MODEL_AMPERE && model != MMAEMU_MODEL_HOPPER) return MMAEMU_ERR_MODEL;
+  if (model != MMAEMU_MODEL_AMPERE && model != MMAEMU_MODEL_HOPPER &&
+      model != MMAEMU_MODEL_LOVELACE)
+    return MMAEMU_ERR_MODEL;
   if (dtype != MMAEMU_DTYPE_FP16 && dtype != MMAEMU_DTYPE_BF16 &&
       dtype != MMAEMU_DTYPE_FP8_E4M3)
     return MMAEMU_ERR_DTYPE;
@@ -255,8 +257,9 @@ hipError_t launch_tiles(const void* A, const void* B, const uint32_t* C, uint32_
   return hipGetLastError();
 }
 
+// LOVELACE runs the Ampere kernels (see the model enum in mmaemu.h).
 #define MMAEMU_DISPATCH(model, dtype, FN, ...)                                  \
-  ((model) == MMAEMU_MODEL_AMPERE                                               \
+  ((model) == MMAEMU_MODEL_AMPERE || (model) == MMAEMU_MODEL_LOVELACE           \
        ? ((dtype) == MMAEMU_DTYPE_FP16 ? FN<kAmpere, kFP16>(__VA_ARGS__)        \
                                        : FN<kAmpere, kBF16>(__VA_ARGS__))       \
        : ((dtype) == MMAEMU_DTYPE_FP16                                          \

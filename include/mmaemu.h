@@ -74,8 +74,14 @@
 extern "C" {
 #endif
 
-/* arithmetic models: the architectures the Hawkeye study characterised */
-enum { MMAEMU_MODEL_AMPERE = 0, MMAEMU_MODEL_HOPPER = 1 };
+/* arithmetic models: the architectures the Hawkeye study characterised.
+ * LOVELACE computes exactly as AMPERE: the pages report its MMA to have
+ * Ampere's structure ("Recovered Ampere FP16 pipeline").  Caveat: they
+ * also cite an FP16 product that comes out differently on an L40S and an
+ * A100 and keep two simulators ("Problem and motivation", "Experiments and
+ * results"), but print nothing that tells the two apart, so no difference
+ * is modelled.  FP8 E4M3 is not accepted with LOVELACE. */
+enum { MMAEMU_MODEL_AMPERE = 0, MMAEMU_MODEL_HOPPER = 1, MMAEMU_MODEL_LOVELACE = 2 };
 
 /* input formats: FP16, BF16 and FP8 E4M3 ("One-sentence summary") */
 enum { MMAEMU_DTYPE_FP16 = 0, MMAEMU_DTYPE_BF16 = 1, MMAEMU_DTYPE_FP8_E4M3 = 2 };
@@ -84,7 +90,7 @@ enum {
   MMAEMU_OK = 0,
   MMAEMU_ERR_MODEL = -1,       /* unknown model */
   MMAEMU_ERR_DTYPE = -2,       /* unknown dtype */
-  MMAEMU_ERR_UNSUPPORTED = -3, /* E4M3 with the Ampere model */
+  MMAEMU_ERR_UNSUPPORTED = -3, /* E4M3 with a model other than Hopper */
   MMAEMU_ERR_SHAPE = -4,       /* negative size, K not a multiple of 16, overflow */
   MMAEMU_ERR_NULL = -5,        /* a required pointer is NULL */
   MMAEMU_ERR_ALIAS = -6,       /* buffers overlap other than D == C */

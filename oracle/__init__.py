@@ -22,10 +22,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "mma_oracle.c")
 LIB = os.path.join(HERE, "liboracle.so")
 
-AMPERE, HOPPER = 0, 1
+AMPERE, HOPPER, LOVELACE = 0, 1, 2
 FP16, BF16, E4M3 = 0, 1, 2
 
-MODELS = {"ampere": AMPERE, "hopper": HOPPER}
+MODELS = {"ampere": AMPERE, "hopper": HOPPER, "lovelace": LOVELACE}
 DTYPES = {"fp16": FP16, "bf16": BF16, "e4m3": E4M3}
 CODE_DTYPE = {FP16: np.uint16, BF16: np.uint16, E4M3: np.uint8}
 

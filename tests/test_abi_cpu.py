@@ -44,6 +44,8 @@ A, B, C, D, X = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
     ((7, 0, A, B, C, D, 32, 32, 32, X), -1),           # unknown model
     ((0, 9, A, B, C, D, 32, 32, 32, X), -2),           # unknown dtype
     ((0, 2, A, B, C, D, 32, 32, 32, X), -3),           # E4M3 with Ampere
+    ((2, 2, A, B, C, D, 32, 32, 32, X), -3),           # E4M3 with Lovelace
+    ((3, 0, A, B, C, D, 32, 32, 32, X), -1),           # model 3 does not exist
     ((0, 0, A, B, C, D, 32, 32, 24, X), -4),           # K not a multiple of 16
     ((0, 0, A, B, C, D, -1, 32, 32, X), -4),           # negative M
     ((0, 0, A, B, C, D, 1 << 40, 1 << 40, 32, X), -4),  # size overflow

@@ -137,6 +137,26 @@ def _gen(kind, model, dt, M, N, K, seed):
     return I.gemm_specials(seed, M, N, K, DT[dt])
 
 
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_lovelace_gemm_and_tiles(torch_dev, orc, dt):
+    """Lovelace runs the Ampere arithmetic: GEMMs and tiles against the
+    oracle's Lovelace model."""
+    for si, (M, N, K) in enumerate([(17, 33, 48), (130, 100, 160)]):
+        for kind in ("normal", "specials"):
+            A, B, C = _gen(kind, "lovelace", dt, M, N, K, 7000 + si)
+            say("lovelace gemm", dt, kind, (M, N, K))
+            got, gx = run_gemm(torch_dev, "lovelace", dt, A, B, C)
+            want, wx = orc.gemm("lovelace", dt, A, B, C)
+            assert_bits_equal(got, want, f"lovelace {dt}/{kind} {M}x{N}x{K}")
+            assert_bits_equal(gx, wx, f"lovelace xorsum {dt}/{kind} {M}x{N}x{K}")
+    A, B, C = I.tiles_normal(1001, 300) if dt == "fp16" else I.tiles_mixed(2002, 300, I.BF16)
+    D, X = mm.tiles("lovelace", dt, to_dev(torch_dev, A), to_dev(torch_dev, B),
+                    to_dev(torch_dev, C), xorsum=True)
+    want, wx = orc.tiles("lovelace", dt, A, B, C)
+    assert_bits_equal(to_host_bits(D), want, f"lovelace tiles {dt}")
+    assert_bits_equal(to_host_bits(X), wx, f"lovelace tiles xorsum {dt}")
+
+
 @pytest.mark.parametrize("model,dt", COMBOS)
 @pytest.mark.parametrize("kind", ["normal", "wide", "specials"])
 def test_gemm_small_full_compare(torch_dev, orc, model, dt, kind):
