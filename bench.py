@@ -8,7 +8,9 @@ step, per-row xorsum fingerprint), inputs resident in HBM before the timed
 region starts.  --workload selects the BF16 or E4M3 Hopper-model GEMM of the
 same size instead.  --verify times the audit compare (mma_verify_gemm: the
 same emulation, compared bit for bit with a claimed D instead of stored)
-against a claimed D equal to the oracle's.
+against a claimed D equal to the oracle's.  --splits S times the split-K
+schedule (mma_emulate_gemm_splitk: S runs of K/(16 S) steps, partial
+results added in FP32 round-to-nearest-even).
 
 Prints ONE JSON line.  --gpus above 1 is refused (one GPU per process and
 box; the path shards over rows of D, see the design notes).
@@ -75,6 +77,8 @@ def parse():
     p.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD)
     p.add_argument("--verify", action="store_true",
                    help="time the audit compare against a claimed D instead of the GEMM")
+    p.add_argument("--splits", type=int, default=1,
+                   help="split-K schedule with this many runs (a divisor of K/16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU work for the oracle sample")
@@ -119,7 +123,12 @@ def main():
     import bit_exact_matrix_amd as mm
     from bit_exact_matrix_amd import inputs as I
 
+    if args.splits < 1 or (K // 16) % args.splits or (args.verify and args.splits != 1):
+        print("--splits must divide K/16 = 256 and cannot be combined with --verify",
+              file=sys.stderr)
+        sys.exit(2)
     model, model_id, dtname, dt_id, (gen, seed), data, pages_s = WORKLOADS[args.workload]
+    suffix = f"_splitk{args.splits}" if args.splits > 1 else ""
     mm.load_library()
     dev = torch.device("cuda:0")
     A, B, C = getattr(I, gen)(seed, M, N, K)
@@ -133,14 +142,20 @@ def main():
 
     # one launch = the whole hot path (with the xorsum epilogue)
     def emulate():
-        rc = mm.mma_emulate_gemm_async(model_id, dt_id, tA.data_ptr(), tB.data_ptr(),
-                                       tC.data_ptr(), tD.data_ptr(), M, N, K, tX.data_ptr(),
-                                       stream.cuda_stream)
+        if args.splits == 1:
+            rc = mm.mma_emulate_gemm_async(model_id, dt_id, tA.data_ptr(), tB.data_ptr(),
+                                           tC.data_ptr(), tD.data_ptr(), M, N, K,
+                                           tX.data_ptr(), stream.cuda_stream)
+        else:
+            rc = mm.mma_emulate_gemm_splitk_async(model_id, dt_id, tA.data_ptr(),
+                                                  tB.data_ptr(), tC.data_ptr(), tD.data_ptr(),
+                                                  M, N, K, args.splits, tX.data_ptr(),
+                                                  stream.cuda_stream)
         if rc:
             raise mm.MmaEmuError(rc, "mma_emulate_gemm_async")
 
     dig = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))
-    ref = dig.get(DIGEST_KEY[args.workload], {})
+    ref = dig.get(DIGEST_KEY[args.workload] + suffix, {})
     one = emulate
     if args.verify:
         # the claimed D: the emulated one, whose digest must be the oracle's
@@ -214,8 +229,8 @@ def main():
     alg = ALG_SLOTS_PER_MAC[model]
     achieved = alg * MACS / avg_launch_s
     khash = kernel_source_hash()
-    hbm_name, valu_name = (None, None) if args.verify else PROFILES.get(args.workload,
-                                                                        (None, None))
+    hbm_name, valu_name = ((None, None) if args.verify or suffix
+                           else PROFILES.get(args.workload, (None, None)))
     hbm = profile_record(hbm_name, khash) if hbm_name else None
     valu = profile_record(valu_name, khash) if valu_name else None
     roofline = {"bound": "alu", "achieved": round(achieved / 1e12, 3),
@@ -238,13 +253,18 @@ def main():
         oracle.build(force=False)
         nth = max(1, min(args.cpu_threads, oracle.num_cpus()))
         # calibrate on a few rows, then time a sample worth ~cpu_seconds
+        def rows_of(n):
+            if args.splits > 1:   # the split-K schedule on the first n rows
+                return oracle.gemm_splitk(model, dtname, A[:n], B, C[:n], args.splits,
+                                          nthreads=nth)
+            return oracle.gemm_rows(model, dtname, A, B, C, 0, n, nthreads=nth)
         t = time.perf_counter()
-        oracle.gemm_rows(model, dtname, A, B, C, 0, nth, nthreads=nth)
+        rows_of(nth)
         per_row = (time.perf_counter() - t) / nth
         rows = int(max(nth, min(M, args.cpu_seconds / max(per_row, 1e-9))))
         rows = max(nth, (rows // nth) * nth)
         t = time.perf_counter()
-        Dr, Xr = oracle.gemm_rows(model, dtname, A, B, C, 0, rows, nthreads=nth)
+        Dr, Xr = rows_of(rows)
         cs = time.perf_counter() - t
         cpu = {"value": round(rows * N * K / cs, 1), "unit": "MAC/s", "cores": nth,
                "kind": "oracle", "seconds": round(cs, 2),
@@ -254,7 +274,9 @@ def main():
 
     out = {
         "metric": (f"bit-exact {'audit-compare' if args.verify else 'emulated'} MACs/s, "
-                   f"4096³ {dtname.upper()} {model.capitalize()} model; % of VALU peak"),
+                   f"4096³ {dtname.upper()} {model.capitalize()} model"
+                   + (f", split-K {args.splits}" if args.splits > 1 else "")
+                   + "; % of VALU peak"),
         "value": round(value, 1),
         "unit": "MAC/s",
         "n_gpus": 1,
@@ -266,7 +288,7 @@ def main():
         "vs_baseline": round(value / (MACS / pages_s), 1),
         "dtype": "int32",
         "data": data,
-        "config": {"workload": args.workload + ("_verify" if args.verify else ""),
+        "config": {"workload": args.workload + ("_verify" if args.verify else "") + suffix,
                    "M": M, "N": N, "K": K, "model": model,
                    "input": dtname, "accumulator": "fp32", "xorsum": "per-row",
                    "parallelism": "single-gpu"},

@@ -7,11 +7,12 @@ CPU fallback: if the library is missing or no GPU is present, the calls
 raise.
 
 The raw C entry points are available under their own names
-(``mma_emulate_gemm``, ``mma_emulate_gemm_async``, ``mma_verify_gemm``,
-``mma_verify_gemm_async``, ``mma_emulate_tiles``, ``mma_emulate_strerror``,
-``mma_emulate_spec_version``) and take integers (device pointers) exactly as
-the C functions do; ``gemm``, ``verify`` and ``tiles`` wrap them for torch
-tensors.
+(``mma_emulate_gemm``, ``mma_emulate_gemm_async``,
+``mma_emulate_gemm_splitk``, ``mma_emulate_gemm_splitk_async``,
+``mma_verify_gemm``, ``mma_verify_gemm_async``, ``mma_emulate_tiles``,
+``mma_emulate_strerror``, ``mma_emulate_spec_version``) and take integers
+(device pointers) exactly as the C functions do; ``gemm``, ``verify`` and
+``tiles`` wrap them for torch tensors.
 """
 from __future__ import annotations
 
@@ -25,9 +26,9 @@ AMPERE, HOPPER, LOVELACE = 0, 1, 2
 FP16, BF16, FP8_E4M3 = 0, 1, 2
 MODELS = {"ampere": AMPERE, "hopper": HOPPER, "lovelace": LOVELACE}
 DTYPES = {"fp16": FP16, "bf16": BF16, "e4m3": FP8_E4M3, "fp8_e4m3": FP8_E4M3}
-EXPORTED = ("mma_emulate_gemm", "mma_emulate_gemm_async", "mma_verify_gemm",
-            "mma_verify_gemm_async", "mma_emulate_tiles", "mma_emulate_strerror",
-            "mma_emulate_spec_version")
+EXPORTED = ("mma_emulate_gemm", "mma_emulate_gemm_async", "mma_emulate_gemm_splitk",
+            "mma_emulate_gemm_splitk_async", "mma_verify_gemm", "mma_verify_gemm_async",
+            "mma_emulate_tiles", "mma_emulate_strerror", "mma_emulate_spec_version")
 
 
 class MmaEmuError(RuntimeError):
@@ -49,6 +50,10 @@ def load_library(path: str = LIB_PATH):
         vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         lib.mma_emulate_gemm.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp]
         lib.mma_emulate_gemm_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp]
+        lib.mma_emulate_gemm_splitk.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, i64,
+                                                vp]
+        lib.mma_emulate_gemm_splitk_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64,
+                                                      i64, vp, vp]
         lib.mma_verify_gemm.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp]
         lib.mma_verify_gemm_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp,
                                               vp]
@@ -56,7 +61,9 @@ def load_library(path: str = LIB_PATH):
         lib.mma_emulate_strerror.argtypes = [i32]
         lib.mma_emulate_strerror.restype = ctypes.c_char_p
         lib.mma_emulate_spec_version.argtypes = []
-        for f in (lib.mma_emulate_gemm, lib.mma_emulate_gemm_async, lib.mma_verify_gemm,
+        for f in (lib.mma_emulate_gemm, lib.mma_emulate_gemm_async,
+                  lib.mma_emulate_gemm_splitk, lib.mma_emulate_gemm_splitk_async,
+                  lib.mma_verify_gemm,
                   lib.mma_verify_gemm_async, lib.mma_emulate_tiles,
                   lib.mma_emulate_spec_version):
             f.restype = i32
@@ -72,6 +79,17 @@ def mma_emulate_gemm(model, dtype, A, B, C, D, M, N, K, xorsum_out):
 def mma_emulate_gemm_async(model, dtype, A, B, C, D, M, N, K, xorsum_out, hip_stream):
     return load_library().mma_emulate_gemm_async(model, dtype, A, B, C, D, M, N, K,
                                                  xorsum_out, hip_stream)
+
+
+def mma_emulate_gemm_splitk(model, dtype, A, B, C, D, M, N, K, splits, xorsum_out):
+    return load_library().mma_emulate_gemm_splitk(model, dtype, A, B, C, D, M, N, K, splits,
+                                                  xorsum_out)
+
+
+def mma_emulate_gemm_splitk_async(model, dtype, A, B, C, D, M, N, K, splits, xorsum_out,
+                                  hip_stream):
+    return load_library().mma_emulate_gemm_splitk_async(model, dtype, A, B, C, D, M, N, K,
+                                                        splits, xorsum_out, hip_stream)
 
 
 def mma_verify_gemm(model, dtype, A, B, C, D_claimed, M, N, K, report, row_diff_out):
@@ -127,11 +145,12 @@ def _stream_handle(stream):
     return s.cuda_stream
 
 
-def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
+def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None, splits=1):
     """Emulated D = C + A.B on the current stream.
 
     A: M x K and B: K x N device tensors of raw codes (2-byte elements for
     FP16/BF16, 1-byte for E4M3).  C: optional M x N float32 (bit patterns).
+    splits > 1 selects the split-K schedule (mma_emulate_gemm_splitk).
     Returns (D, xorsum): D float32 M x N, xorsum int32 of M words (bit
     patterns of the per-row XOR) or None.
     """
@@ -147,11 +166,12 @@ def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
     if D is None:
         D = torch.empty((M, N), dtype=torch.float32, device=A.device)
     X = torch.empty(M, dtype=torch.int32, device=A.device) if xorsum else None
-    rc = mma_emulate_gemm_async(m, d, _dev_ptr(A, "A", esz), _dev_ptr(B, "B", esz),
-                                _dev_ptr(C, "C", 4), _dev_ptr(D, "D", 4), M, N, K,
-                                _dev_ptr(X, "xorsum"), _stream_handle(stream))
+    rc = mma_emulate_gemm_splitk_async(m, d, _dev_ptr(A, "A", esz), _dev_ptr(B, "B", esz),
+                                       _dev_ptr(C, "C", 4), _dev_ptr(D, "D", 4), M, N, K,
+                                       int(splits), _dev_ptr(X, "xorsum"),
+                                       _stream_handle(stream))
     if rc != 0:
-        raise MmaEmuError(rc, "mma_emulate_gemm_async")
+        raise MmaEmuError(rc, "mma_emulate_gemm_splitk_async")
     return D, X
 
 

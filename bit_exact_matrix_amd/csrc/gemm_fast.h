@@ -619,20 +619,23 @@ constexpr int kWavesPerSimd = DMA ? 3 : 2;
 
 // DMA = true: the operand images come from the pre-pass workspace (ws_a,
 // ws_b) by direct global->LDS copies; DMA = false: the kernel builds them
-// from the raw codes (no workspace).  The K loop is unrolled twice so that
-// the accumulator state alternates between two register sets instead of
-// being copied back every step.
+// from the raw codes (no workspace).  The kernel chains the ns steps that
+// start at step s0 (all K/16 of them for a plain GEMM, one run of a split-K
+// schedule otherwise).  The K loop is unrolled twice so that the
+// accumulator state alternates between two register sets instead of being
+// copied back every step.
 template <int MODEL, int DT, bool DMA>
 __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
-    int64_t M, int64_t N, int64_t K, const uint32_t* __restrict__ ws_a,
-    const uint32_t* __restrict__ ws_b) {
+    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns,
+    const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b) {
   __shared__ Stage stage[2];
   const int t = threadIdx.x;
   const int ty = t >> 4, tx = t & 15;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int64_t bm = (int64_t)blockIdx.y * BM, bn = (int64_t)blockIdx.x * BN;
-  const int64_t nsteps = K / 16;
+  const int64_t nsteps = ns;           // steps chained here
+  const int64_t total = K / 16;        // steps of the whole GEMM (image stride)
 
   int X[4][4], Xn[4][4];
   uint32_t NE[2][4], NEn[2][4];
@@ -650,15 +653,18 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
       NE[q][c] = ne[0] | ne[1] << 16;
     }
 
-  const uint32_t* img_a = DMA ? ws_a + (int64_t)blockIdx.y * nsteps * IMG_WORDS : nullptr;
-  const uint32_t* img_b = DMA ? ws_b + (int64_t)blockIdx.x * nsteps * IMG_WORDS : nullptr;
+  const uint32_t* img_a =
+      DMA ? ws_a + ((int64_t)blockIdx.y * total + s0) * IMG_WORDS : nullptr;
+  const uint32_t* img_b =
+      DMA ? ws_b + ((int64_t)blockIdx.x * total + s0) * IMG_WORDS : nullptr;
   uint32_t ca[4], cb[4];
-  // fill of stage s: start it (before the previous step's compute), end it
+  // fill of stage s (local step s, absolute step s0 + s): start it (before
+  // the previous step's compute), end it
   auto begin_fill = [&](int64_t s) {
     if constexpr (DMA) {
       dma_step(&stage[s & 1], img_a + s * IMG_WORDS, img_b + s * IMG_WORDS, w, lane);
     } else {
-      fetch<DT>(A, B, M, N, K, bm, bn, s, t, ca, cb);
+      fetch<DT>(A, B, M, N, K, bm, bn, s0 + s, t, ca, cb);
     }
   };
   auto end_fill = [&](int64_t s) {
@@ -676,7 +682,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
 
   for (int64_t s = 0; s < nsteps; s += 2) {
     if (s + 1 < nsteps) begin_fill(s + 1);
-    tile_step<MODEL, DT>(&stage[s & 1], ty, tx, A, B, M, N, K, s, X, NE, Xn, NEn);
+    tile_step<MODEL, DT>(&stage[s & 1], ty, tx, A, B, M, N, K, s0 + s, X, NE, Xn, NEn);
     if (s + 1 < nsteps) end_fill(s + 1);
     __syncthreads();
     if (s + 1 >= nsteps) {
@@ -691,7 +697,8 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
       break;
     }
     if (s + 2 < nsteps) begin_fill(s + 2);
-    tile_step<MODEL, DT>(&stage[(s + 1) & 1], ty, tx, A, B, M, N, K, s + 1, Xn, NEn, X, NE);
+    tile_step<MODEL, DT>(&stage[(s + 1) & 1], ty, tx, A, B, M, N, K, s0 + s + 1, Xn, NEn, X,
+                         NE);
     if (s + 2 < nsteps) end_fill(s + 2);
     __syncthreads();
   }
@@ -721,8 +728,9 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
             first = (unsigned long long)idx < first ? (unsigned long long)idx : first;
           }
         } else {
-          out.D[idx] = d;
-          rowx[r] ^= d;
+          const uint32_t v = out.accumulate ? fp32_add_rne(out.D[idx], d) : d;
+          out.D[idx] = v;
+          rowx[r] ^= v;
         }
       }
     }
@@ -755,24 +763,38 @@ inline int64_t gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 }
 
 // ws: NULL for the in-kernel image build, else gemm_fast_workspace_bytes() bytes.
+// splits > 1 (a divisor of K/16): the split-K schedule.  Run r chains steps
+// [r*T/splits, (r+1)*T/splits) of the T = K/16 steps, from C for r = 0 and
+// from +0 otherwise; the runs are launched in order and each later one adds
+// its partial result into D (fp32_add_rne), so that D = ((P0 + P1) + P2)...
+// The xorsum, if any, is taken by the last run, over the final D.
 template <int MODEL, int DT>
 inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, const Sink& out,
-                             int64_t M, int64_t N, int64_t K, void* ws, hipStream_t s) {
+                             int64_t M, int64_t N, int64_t K, void* ws, hipStream_t s,
+                             int64_t splits = 1) {
   const int64_t mb = (M + fastk::BM - 1) / fastk::BM, nb = (N + fastk::BN - 1) / fastk::BN;
-  const int64_t nsteps = K / 16;
+  const int64_t nsteps = K / 16, per = nsteps / splits;
   const dim3 grid((unsigned)nb, (unsigned)mb);
+  uint32_t* ws_a = (uint32_t*)ws;
+  uint32_t* ws_b = ws ? ws_a + mb * nsteps * fastk::IMG_WORDS : nullptr;
   if (ws) {
-    uint32_t* ws_a = (uint32_t*)ws;
-    uint32_t* ws_b = ws_a + mb * nsteps * fastk::IMG_WORDS;
     fastk::unpack_kernel<MODEL, DT, false>
         <<<dim3((unsigned)nsteps, (unsigned)mb), dim3(64), 0, s>>>(A, M, K, N, nsteps, ws_a);
     fastk::unpack_kernel<MODEL, DT, true>
         <<<dim3((unsigned)nsteps, (unsigned)nb), dim3(64), 0, s>>>(B, N, K, N, nsteps, ws_b);
-    fastk::gemm_fast_kernel<MODEL, DT, true>
-        <<<grid, dim3(fastk::NT), 0, s>>>(A, B, C, out, M, N, K, ws_a, ws_b);
-  } else {
-    fastk::gemm_fast_kernel<MODEL, DT, false>
-        <<<grid, dim3(fastk::NT), 0, s>>>(A, B, C, out, M, N, K, nullptr, nullptr);
+  }
+  for (int64_t r = 0; r < splits; ++r) {
+    Sink o = out;
+    o.accumulate = r > 0;
+    if (r + 1 < splits) o.xorsum = nullptr;
+    const uint32_t* c = r == 0 ? C : nullptr;
+    if (ws) {
+      fastk::gemm_fast_kernel<MODEL, DT, true>
+          <<<grid, dim3(fastk::NT), 0, s>>>(A, B, c, o, M, N, K, r * per, per, ws_a, ws_b);
+    } else {
+      fastk::gemm_fast_kernel<MODEL, DT, false>
+          <<<grid, dim3(fastk::NT), 0, s>>>(A, B, c, o, M, N, K, r * per, per, nullptr, nullptr);
+    }
   }
 }
 

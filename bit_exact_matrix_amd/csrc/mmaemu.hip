@@ -55,12 +55,13 @@ __global__ __launch_bounds__(256) void tiles_kernel(const void* __restrict__ A,
 }
 
 // --------------------------------------------------- reference GEMM path
-// One lane per output, 256 chained steps read straight from global memory.
-// Kept as the simple, fully general path (any shape, any input bits).
+// One lane per output, the chained steps read straight from global memory.
+// Kept as the simple, fully general path (any shape, any input bits).  It
+// chains the ns steps that start at step s0.
 template <int MODEL, int DT>
 __global__ __launch_bounds__(256) void gemm_reference_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
-    int64_t M, int64_t N, int64_t K) {
+    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns) {
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool live = col < N;
   uint32_t nbad = 0;
@@ -69,7 +70,7 @@ __global__ __launch_bounds__(256) void gemm_reference_kernel(
     uint32_t c = 0, x = 0;
     if (live) {
       c = C ? C[row * N + col] : 0u;
-      for (int64_t t = 0; t < K / 16; ++t) {
+      for (int64_t t = s0; t < s0 + ns; ++t) {
         uint32_t a[16], b[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -86,8 +87,8 @@ __global__ __launch_bounds__(256) void gemm_reference_kernel(
           first = (unsigned long long)idx < first ? (unsigned long long)idx : first;
         }
       } else {
-        out.D[idx] = c;
-        x = c;
+        x = out.accumulate ? fp32_add_rne(out.D[idx], c) : c;
+        out.D[idx] = x;
       }
     }
     if (out.xorsum) {
@@ -224,7 +225,7 @@ void* workspace_alloc(int64_t bytes, hipStream_t s) {
 
 template <int MODEL, int DT>
 hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Sink& out,
-                       int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                       int64_t M, int64_t N, int64_t K, hipStream_t s, int64_t splits = 1) {
   if (out.xorsum && M > 0) {
     const int64_t blocks = (M + 255) / 256;
     fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(out.xorsum, M);
@@ -233,7 +234,7 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
   if (M == 0 || N == 0) return hipGetLastError();
   if (gemm_fast_supported(M, N, K)) {
     void* ws = workspace_alloc(gemm_fast_workspace_bytes(M, N, K), s);
-    gemm_fast_launch<MODEL, DT>(A, B, C, out, M, N, K, ws, s);
+    gemm_fast_launch<MODEL, DT>(A, B, C, out, M, N, K, ws, s, splits);
     if (ws) {
       // the free is ordered after the kernels; it is issued whatever the
       // launches returned, so that a failed call does not hold the memory
@@ -244,8 +245,14 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
   } else {
     const int64_t cb = (N + 255) / 256;
     const int64_t rows = M < 32768 ? M : 32768;
-    gemm_reference_kernel<MODEL, DT>
-        <<<dim3((unsigned)cb, (unsigned)rows), dim3(256), 0, s>>>(A, B, C, out, M, N, K);
+    const int64_t per = K / 16 / splits;
+    for (int64_t r = 0; r < splits; ++r) {
+      Sink o = out;
+      o.accumulate = r > 0;
+      if (r + 1 < splits) o.xorsum = nullptr;
+      gemm_reference_kernel<MODEL, DT><<<dim3((unsigned)cb, (unsigned)rows), dim3(256), 0, s>>>(
+          A, B, r == 0 ? C : nullptr, o, M, N, K, r * per, per);
+    }
   }
   return hipGetLastError();
 }
@@ -285,12 +292,14 @@ int check_gemm_shape(int dtype, int64_t M, int64_t N, int64_t K, GemmBytes* g) {
 
 int gemm_impl(int model, int dtype, const void* A, const void* B, const float* C,
               float* D, int64_t M, int64_t N, int64_t K, uint32_t* xorsum,
-              hipStream_t s) {
+              hipStream_t s, int64_t splits = 1) {
   int rc = check_model_dtype(model, dtype);
   if (rc) return rc;
   GemmBytes g;
   rc = check_gemm_shape(dtype, M, N, K, &g);
   if (rc) return rc;
+  // split-K: a whole number of steps per run
+  if (splits < 1 || (K == 0 ? splits != 1 : (K / 16) % splits != 0)) return MMAEMU_ERR_SHAPE;
   // an empty D: nothing to compute; the xorsum words of its M empty rows
   // are still written (as zeros)
   if (g.cd == 0 && !(xorsum && M > 0)) return MMAEMU_OK;
@@ -298,9 +307,9 @@ int gemm_impl(int model, int dtype, const void* A, const void* B, const float* C
   rc = check_alias(g.cd && K ? A : nullptr, g.a, g.cd && K ? B : nullptr, g.b,
                    g.cd ? C : nullptr, g.cd ? D : nullptr, g.cd, xorsum, xorsum ? M * 4 : 0);
   if (rc) return rc;
-  const Sink out{(uint32_t*)D, xorsum, nullptr, nullptr};
-  const hipError_t e =
-      MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C, out, M, N, K, s);
+  const Sink out{(uint32_t*)D, xorsum, nullptr, nullptr, 0};
+  const hipError_t e = MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C,
+                                       out, M, N, K, s, splits);
   if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm launch");
   return MMAEMU_OK;
 }
@@ -320,7 +329,8 @@ int verify_impl(int model, int dtype, const void* A, const void* B, const float*
                           any ? C : nullptr, any ? D_claimed : nullptr, g.cd, report,
                           row_diff, row_diff ? M * 4 : 0);
   if (rc) return rc;
-  const Sink out{nullptr, row_diff, (const uint32_t*)D_claimed, (unsigned long long*)report};
+  const Sink out{nullptr, row_diff, (const uint32_t*)D_claimed, (unsigned long long*)report,
+                 0};
   const hipError_t e =
       MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C, out, M, N, K, s);
   if (e != hipSuccess) return hip_fail(e, "mma_verify_gemm launch");
@@ -343,6 +353,23 @@ int mma_emulate_gemm(int model, int dtype, const void* A, const void* B, const f
   if (rc) return rc;
   const hipError_t e = hipStreamSynchronize(nullptr);
   if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm synchronize");
+  return MMAEMU_OK;
+}
+
+int mma_emulate_gemm_splitk_async(int model, int dtype, const void* A, const void* B,
+                                  const float* C, float* D, int64_t M, int64_t N, int64_t K,
+                                  int64_t splits, uint32_t* xorsum_out, void* hip_stream) {
+  return gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, (hipStream_t)hip_stream,
+                   splits);
+}
+
+int mma_emulate_gemm_splitk(int model, int dtype, const void* A, const void* B,
+                            const float* C, float* D, int64_t M, int64_t N, int64_t K,
+                            int64_t splits, uint32_t* xorsum_out) {
+  const int rc = gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, nullptr, splits);
+  if (rc) return rc;
+  const hipError_t e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm_splitk synchronize");
   return MMAEMU_OK;
 }
 

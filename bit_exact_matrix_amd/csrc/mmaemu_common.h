@@ -265,12 +265,23 @@ __device__ __forceinline__ uint32_t wave_xor(uint32_t v) {
 //   elements and report[1] keeps the smallest mismatching row-major index
 //   (both set up by the host before the kernel: 0 and all ones); xorsum, if
 //   not NULL, receives the XOR over each row of (result ^ claimed).
+//   accumulate (store mode only): D receives fp32_add_rne(D, result)
+//   instead of the result: the split-K reduction of partial results.
 struct Sink {
   uint32_t* D;
   uint32_t* xorsum;
   const uint32_t* claimed;
   unsigned long long* report;
+  int accumulate;
 };
+
+// IEEE-754 binary32 addition rounding to nearest, ties to even, with
+// subnormals kept (the hardware add; no flush to zero is enabled for this
+// code) and every NaN result replaced by the canonical 0x7FC00000.
+__device__ __forceinline__ uint32_t fp32_add_rne(uint32_t a, uint32_t b) {
+  const float r = __fadd_rn(__uint_as_float(a), __uint_as_float(b));
+  return r != r ? 0x7FC00000u : __float_as_uint(r);
+}
 
 // Folds one lane's mismatch count and smallest mismatching index into the
 // report, once per wavefront.  Every lane of the wavefront must call it.

@@ -62,8 +62,9 @@
  *
  * DETERMINISM
  *   The same inputs give the same D and xorsum bits on every call, stream
- *   and device.  Each D element is written by exactly one lane; there is no
- *   split-K and no atomic accumulation of D.
+ *   and device.  Each D element is written by exactly one lane (per run of
+ *   the split-K schedule, whose runs execute in order); there is no atomic
+ *   accumulation of D.
  */
 #ifndef MMAEMU_H
 #define MMAEMU_H
@@ -109,6 +110,34 @@ int mma_emulate_gemm(int model, int dtype, const void *A, const void *B,
 int mma_emulate_gemm_async(int model, int dtype, const void *A, const void *B,
                            const float *C, float *D, int64_t M, int64_t N,
                            int64_t K, uint32_t *xorsum_out, void *hip_stream);
+
+/* Split-K schedule, an explicit model input.  The pages name split-K (and
+ * atomic accumulation) as ways a production library may compose tiles
+ * differently from a chain of isolated MMA steps, and leave its
+ * characterisation open (Hawkeye notes, "Critical Analysis": the
+ * assumption stress test, the missing production path, Future work 4).
+ * This entry point fixes one deterministic schedule:
+ *   the T = K/16 steps are cut into `splits` runs of T/splits consecutive
+ *   steps (splits must divide T; splits = 1 is mma_emulate_gemm_async);
+ *   run r chains its steps as mma_emulate_gemm does, starting from C for
+ *   r = 0 and from +0 for r > 0, giving the FP32 partial result P_r;
+ *   D = (((P_0 + P_1) + P_2) + ... + P_{splits-1}), each addition an
+ *   IEEE-754 binary32 addition rounding to nearest, ties to even, with
+ *   subnormals kept; a NaN result is the canonical 0x7FC00000.
+ * The xorsum fingerprint is taken over the final D.  Arguments, layouts,
+ * aliasing (D == C allowed), workspace and errors as for
+ * mma_emulate_gemm_async; splits < 1 or not dividing K/16 (or splits != 1
+ * with K = 0) is MMAEMU_ERR_SHAPE.  Enqueued on hip_stream; returns after
+ * enqueue. */
+int mma_emulate_gemm_splitk_async(int model, int dtype, const void *A,
+                                  const void *B, const float *C, float *D,
+                                  int64_t M, int64_t N, int64_t K, int64_t splits,
+                                  uint32_t *xorsum_out, void *hip_stream);
+
+/* Same contract, blocking (null stream, then synchronised). */
+int mma_emulate_gemm_splitk(int model, int dtype, const void *A, const void *B,
+                            const float *C, float *D, int64_t M, int64_t N,
+                            int64_t K, int64_t splits, uint32_t *xorsum_out);
 
 /* Audit compare: the auditor's side of the Hawkeye workflow (Hawkeye notes,
  * "Problem and motivation" and "Relation to the verifiable-ML workflow": an

@@ -118,6 +118,36 @@ def gemm(model, dtype, A, B, C=None, nthreads=0, xorsum=True, lib=None):
     return D, x
 
 
+def gemm_splitk(model, dtype, A, B, C, splits, nthreads=0, lib=None):
+    """The split-K schedule: the K/16 steps cut into `splits` runs of equal
+    length; run r is the chained GEMM over its K range, from C for r = 0 and
+    from +0 otherwise; D is the sum of the runs' FP32 results in run order,
+    each addition IEEE binary32 round-to-nearest-even (numpy float32), with
+    NaN results written as 0x7FC00000.  Returns (D bits, per-row xorsum).
+    This schedule is a reading: the pages name split-K as a production
+    schedule whose order they did not characterise (Hawkeye notes, "Critical
+    Analysis" and Future work 4)."""
+    M, K = A.shape
+    T = K // 16
+    assert splits >= 1 and K % 16 == 0 and (T % splits == 0 if K else splits == 1)
+    per = 16 * (T // splits) if K else 0
+    acc = None
+    for r in range(splits):
+        P, _ = gemm(model, dtype, A[:, r * per:(r + 1) * per], B[r * per:(r + 1) * per, :],
+                    C if r == 0 else None, nthreads=nthreads, xorsum=False, lib=lib)
+        if acc is None:
+            acc = P
+        else:
+            with np.errstate(invalid="ignore", over="ignore"):
+                s = acc.view(np.float32) + P.view(np.float32)
+            acc = s.view(np.uint32).copy()
+            acc[np.isnan(s)] = 0x7FC00000
+    x = np.zeros(M, np.uint32)
+    for j in range(acc.shape[1]):
+        x ^= acc[:, j]
+    return acc, x
+
+
 def compare(D, D_claimed):
     """Bitwise comparison of an emulated D with a claimed one (both M x N
     bit patterns): (number of differing elements, smallest differing

@@ -25,7 +25,8 @@ def sha(a):
 
 
 def workloads():
-    """name -> (kind, model, dtype, generator) for the five seeded configs."""
+    """name -> (kind, model, dtype, generator) for the five seeded configs
+    (and the 4096^3 FP16 Ampere GEMM under the 4-run split-K schedule)."""
     return {
         "tiles_fp16_1k_ampere": ("tiles", "ampere", "fp16", lambda: I.tiles_normal(1001, 1000)),
         "tiles_mixed_100k_fp16_ampere": ("tiles", "ampere", "fp16",
@@ -42,6 +43,8 @@ def workloads():
                                   lambda: I.gemm_wide_bf16(4001, 4096, 4096, 4096)),
         "gemm_4096_e4m3_hopper": ("gemm", "hopper", "e4m3",
                                   lambda: I.gemm_e4m3(5001, 4096, 4096, 4096)),
+        "gemm_4096_fp16_ampere_splitk4": ("splitk4", "ampere", "fp16",
+                                          lambda: I.gemm_normal(3001, 4096, 4096, 4096)),
     }
 
 
@@ -55,6 +58,8 @@ def main(names):
         t = time.time()
         if kind == "tiles":
             D, x = oracle.tiles(model, dt, A, B, C)
+        elif kind == "splitk4":
+            D, x = oracle.gemm_splitk(model, dt, A, B, C, 4)
         else:
             D, x = oracle.gemm(model, dt, A, B, C)
         dt_s = time.time() - t
