@@ -751,9 +751,12 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
 
 }  // namespace fastk
 
+// Shapes the tiled kernel takes: the GEMM grid is (N blocks, M blocks) and
+// the pre-pass grids are (K/16, M blocks) and (K/16, N blocks), so both
+// block counts must fit gridDim.y (65535) and K/16 gridDim.x.
 inline bool gemm_fast_supported(int64_t M, int64_t N, int64_t K) {
   return M > 0 && N > 0 && K >= 16 && (M + fastk::BM - 1) / fastk::BM <= 65535 &&
-         (N + fastk::BN - 1) / fastk::BN <= INT32_MAX;
+         (N + fastk::BN - 1) / fastk::BN <= 65535 && K / 16 <= INT32_MAX;
 }
 
 // Bytes of pre-pass workspace for an M x N x K GEMM (operand images).
