@@ -226,6 +226,58 @@ def gemm_e4m3(seed: int, M: int, N: int, K: int):
     return A, B, C
 
 
+def gemm_adversarial(seed: int, M: int, N: int, K: int, dtype: int, mode: str = "wide"):
+    """Adversarial GEMM operands.  A, B start from the adversarial element mix
+    (random sign, exponent field uniform over the normal range, 5% subnormal,
+    1% signed zeros; for E4M3 the 254 finite codes); C from the adversarial
+    FP32 mix.  mode:
+      "wide"    as is (products span the whole range; BF16 chains overflow);
+      "narrow"  normal exponents within +-3 of the bias: similar magnitudes;
+      "coarse"  60% of the elements zero, the rest signed powers of two
+                within +-1 of the bias, C a small signed power of two or
+                zero: sums of few signed powers of two, which often cancel
+                exactly;
+      "tiny"    normal exponents in the lowest 6 binades and C among FP32
+                subnormals and zeros: results near or below FP32's normal
+                range."""
+    rng = _rng(seed)
+    if dtype == E4M3:
+        A = e4m3_finite_codes(rng, (M, K))
+        B = e4m3_finite_codes(rng, (K, N))
+    else:
+        A = _adversarial_elements(rng, dtype, (M, K))
+        B = _adversarial_elements(rng, dtype, (K, N))
+    C = _adversarial_c(rng, FP16 if dtype == E4M3 else dtype, (M, N))
+    if mode == "wide":
+        return A, B, C
+    t, e = _GEOM[dtype] if dtype != E4M3 else (3, 4)
+    bias = (1 << (e - 1)) - 1
+    emask = np.uint32(((1 << e) - 1) << t)
+    for X in (A, B):
+        x = X.astype(np.uint32)
+        ef = (x >> t) & ((1 << e) - 1)
+        if mode == "narrow":
+            band = (bias + rng.integers(-3, 4, size=X.shape)).astype(np.uint32)
+        elif mode == "coarse":
+            band = (bias + rng.integers(-1, 2, size=X.shape)).astype(np.uint32)
+        else:  # tiny
+            band = rng.integers(1, 7, size=X.shape).astype(np.uint32)
+        x = np.where(ef != 0, (x & ~emask) | (band << t), x)
+        if mode == "coarse":
+            x = x & ~np.uint32((1 << t) - 1)     # signed powers of two (or zero)
+            x = np.where(rng.random(X.shape) < 0.6, np.uint32(0), x)
+        X[...] = x.astype(X.dtype)
+    if mode == "coarse":
+        pw = (127 + rng.integers(-2, 3, size=C.shape)).astype(np.uint32) << 23
+        sg = rng.integers(0, 2, size=C.shape).astype(np.uint32) << 31
+        C = np.where(rng.random(C.shape) < 0.5, sg | pw, sg).astype(np.uint32)
+    elif mode == "tiny":
+        fr = rng.integers(0, 1 << 23, size=C.shape).astype(np.uint32)
+        sg = rng.integers(0, 2, size=C.shape).astype(np.uint32) << 31
+        C = np.where(rng.random(C.shape) < 0.7, sg | fr, sg).astype(np.uint32)
+    return A, B, C
+
+
 def gemm_specials(seed: int, M: int, N: int, K: int, dtype: int):
     """Normal data sprinkled with inf, NaN, signed zeros and subnormals in A,
     B and C, to exercise the special-value rules (not a pages' workload)."""
