@@ -65,8 +65,8 @@ DIGEST_KEY = {"gemm_4096x4096x4096_fp16_ampere": "gemm_4096_fp16_ampere",
               "gemm_4096x4096x4096_bf16_hopper": "gemm_4096_bf16_hopper",
               "gemm_4096x4096x4096_e4m3_hopper": "gemm_4096_e4m3_hopper"}
 # committed rocprofv3 summaries per workload: (HBM traffic, VALU counters)
-PROFILES = {"gemm_4096x4096x4096_fp16_ampere":
-            ("gemm_4096_fp16_ampere_hbm_traffic.json", "gemm_4096_fp16_ampere_valu_counters.json")}
+PROFILES = {w: (DIGEST_KEY[w] + "_hbm_traffic.json", DIGEST_KEY[w] + "_valu_counters.json")
+            for w in WORKLOADS}
 
 
 def parse():
