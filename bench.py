@@ -64,6 +64,30 @@ DEFAULT_WORKLOAD = "gemm_4096x4096x4096_fp16_ampere"
 DIGEST_KEY = {"gemm_4096x4096x4096_fp16_ampere": "gemm_4096_fp16_ampere",
               "gemm_4096x4096x4096_bf16_hopper": "gemm_4096_bf16_hopper",
               "gemm_4096x4096x4096_e4m3_hopper": "gemm_4096_e4m3_hopper"}
+# Batches of independent 16x16x16 steps (mma_emulate_tiles): name ->
+# (model, model id, dtype name, dtype id, (generator, arguments), input
+# description, stored-digest key)
+TILE_WORKLOADS = {
+    "tiles_1000_fp16_ampere":
+        ("ampere", 0, "fp16", 0, ("tiles_normal", (1001, 1000)),
+         "synthetic: 1000 tiles, A, B FP16 ~N(0,1), C ~N(0,1) seed 1001", "tiles_fp16_1k_ampere"),
+    "tiles_100000_mixed_fp16_ampere":
+        ("ampere", 0, "fp16", 0, ("tiles_mixed", (2001, 100000, 0)),
+         "synthetic: 100000 tiles, half N(0,1), half adversarial, FP16 seed 2001",
+         "tiles_mixed_100k_fp16_ampere"),
+    "tiles_100000_mixed_fp16_hopper":
+        ("hopper", 1, "fp16", 0, ("tiles_mixed", (2001, 100000, 0)),
+         "synthetic: 100000 tiles, half N(0,1), half adversarial, FP16 seed 2001",
+         "tiles_mixed_100k_fp16_hopper"),
+    "tiles_100000_mixed_bf16_ampere":
+        ("ampere", 0, "bf16", 1, ("tiles_mixed", (2002, 100000, 1)),
+         "synthetic: 100000 tiles, half N(0,1), half adversarial, BF16 seed 2002",
+         "tiles_mixed_100k_bf16_ampere"),
+    "tiles_100000_mixed_bf16_hopper":
+        ("hopper", 1, "bf16", 1, ("tiles_mixed", (2002, 100000, 1)),
+         "synthetic: 100000 tiles, half N(0,1), half adversarial, BF16 seed 2002",
+         "tiles_mixed_100k_bf16_hopper"),
+}
 # committed rocprofv3 summaries per workload: (HBM traffic, VALU counters)
 PROFILES = {w: (DIGEST_KEY[w] + "_hbm_traffic.json", DIGEST_KEY[w] + "_valu_counters.json")
             for w in WORKLOADS}
@@ -74,7 +98,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=10)
     p.add_argument("--warmup", type=int, default=3)
-    p.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD)
+    p.add_argument("--workload", choices=sorted(WORKLOADS) + sorted(TILE_WORKLOADS),
+                   default=DEFAULT_WORKLOAD)
     p.add_argument("--verify", action="store_true",
                    help="time the audit compare against a claimed D instead of the GEMM")
     p.add_argument("--splits", type=int, default=1,
@@ -109,6 +134,91 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def bench_tiles(args):
+    """Time one mma_emulate_tiles call per step on a batch of independent
+    16x16x16 steps (the pages' random-tile check); parity by the oracle's
+    stored digests of the whole batch."""
+    import numpy as np
+    import torch
+
+    import bit_exact_matrix_amd as mm
+    from bit_exact_matrix_amd import inputs as I
+
+    model, model_id, dtname, dt_id, (gen, gargs), data, dkey = TILE_WORKLOADS[args.workload]
+    mm.load_library()
+    dev = torch.device("cuda:0")
+    A, B, C = getattr(I, gen)(*gargs)
+    n = A.shape[0]
+    macs = n * 16 * 16 * 16
+    tA = torch.from_numpy(A.view(np.int16)).to(dev)
+    tB = torch.from_numpy(B.view(np.int16)).to(dev)
+    tC = torch.from_numpy(C.view(np.float32)).to(dev)
+    tD = torch.empty((n, 16, 16), dtype=torch.float32, device=dev)
+    tX = torch.empty(n, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one():
+        rc = mm.mma_emulate_tiles(model_id, dt_id, tA.data_ptr(), tB.data_ptr(), tC.data_ptr(),
+                                  tD.data_ptr(), n, tX.data_ptr(), stream.cuda_stream)
+        if rc:
+            raise mm.MmaEmuError(rc, "mma_emulate_tiles")
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        one()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    avg_s = sum(launch_ms) / 1e3 / args.steps
+    D = tD.cpu().numpy().view(np.uint32)
+    X = tX.cpu().numpy().view(np.uint32)
+    ref = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))[dkey]
+    bit_exact = (hashlib.sha256(D.tobytes()).hexdigest() == ref["D_sha256"]
+                 and hashlib.sha256(X.tobytes()).hexdigest() == ref["xorsum_sha256"])
+    achieved = ALG_SLOTS_PER_MAC[model] * macs / avg_s
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.build(force=False)
+        nth = max(1, min(args.cpu_threads, oracle.num_cpus()))
+        t = time.perf_counter()
+        oracle.tiles(model, dtname, A[:1000], B[:1000], C[:1000], nthreads=nth)
+        per = (time.perf_counter() - t) / 1000
+        m = int(max(1000, min(n, args.cpu_seconds / max(per, 1e-9))))
+        t = time.perf_counter()
+        Dr, Xr = oracle.tiles(model, dtname, A[:m], B[:m], C[:m], nthreads=nth)
+        cs = time.perf_counter() - t
+        cpu = {"value": round(m * 4096 / cs, 1), "unit": "MAC/s", "cores": nth,
+               "kind": "oracle", "seconds": round(cs, 2),
+               "sample": f"tiles 0..{m - 1} of the batch",
+               "sample_matches_gpu": bool(np.array_equal(Dr, D[:m]) and np.array_equal(Xr, X[:m]))}
+    out = {
+        "metric": f"bit-exact emulated MACs/s, {n} independent 16x16x16 tiles, "
+                  f"{dtname.upper()} {model.capitalize()} model",
+        "value": round(macs / avg_s, 1), "unit": "MAC/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * avg_s, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": data,
+        "config": {"workload": args.workload, "tiles": n, "model": model, "input": dtname,
+                   "accumulator": "fp32", "xorsum": "per-tile", "parallelism": "single-gpu"},
+        "bit_exact_vs_oracle": bool(bit_exact), "wall_s_timed": round(wall, 4),
+        "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3),
+                     "peak": round(VALU_PEAK_OPS / 1e12, 3), "unit": "TOP/s",
+                     "frac": round(achieved / VALU_PEAK_OPS, 4), "traffic": None,
+                     "alg_slots_per_mac": ALG_SLOTS_PER_MAC[model],
+                     "launch_ms_mean": round(1e3 * avg_s, 4),
+                     "launch_ms_min": round(min(launch_ms), 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -116,6 +226,12 @@ def main():
               "(the GEMM shards over rows of D with no exchange; see the design notes).",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload in TILE_WORKLOADS:
+        if args.verify or args.splits != 1:
+            print("--verify and --splits apply to the GEMM workloads", file=sys.stderr)
+            sys.exit(2)
+        bench_tiles(args)
+        return
 
     import numpy as np
     import torch

@@ -12,47 +12,13 @@
 #include "../../include/mmaemu.h"
 #include "mmaemu_common.h"
 #include "gemm_fast.h"
+#include "tiles_fast.h"
 
 using namespace mmaemu;
 
 namespace {
 
 constexpr int kSpecVersion = 1;
-
-// ------------------------------------------------------------------ tiles
-// One workgroup per 16x16x16 tile, one lane per output element.
-template <int MODEL, int DT>
-__global__ __launch_bounds__(256) void tiles_kernel(const void* __restrict__ A,
-                                                    const void* __restrict__ B,
-                                                    const uint32_t* C,  // may equal D
-                                                    uint32_t* D,
-                                                    uint32_t* __restrict__ xorsum) {
-  __shared__ uint32_t sa[16][17];
-  __shared__ uint32_t sb[16][17];
-  __shared__ uint32_t wx[4];
-  const int64_t tile = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int i = tid >> 4, j = tid & 15;
-  const int64_t base = tile * 256;
-  sa[i][j] = load_code<DT>(A, base + tid);
-  sb[i][j] = load_code<DT>(B, base + tid);
-  const uint32_t c = C ? C[base + tid] : 0u;
-  __syncthreads();
-  uint32_t a[16], b[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) {
-    a[k] = sa[i][k];
-    b[k] = sb[k][j];
-  }
-  const uint32_t d = step_generic<MODEL, DT>(c, a, b);
-  D[base + tid] = d;
-  if (xorsum) {
-    const uint32_t w = wave_xor(d);
-    if ((tid & 63) == 0) wx[tid >> 6] = w;
-    __syncthreads();
-    if (tid == 0) xorsum[tile] = wx[0] ^ wx[1] ^ wx[2] ^ wx[3];
-  }
-}
 
 // --------------------------------------------------- reference GEMM path
 // One lane per output, the chained steps read straight from global memory.
@@ -260,7 +226,11 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
 template <int MODEL, int DT>
 hipError_t launch_tiles(const void* A, const void* B, const uint32_t* C, uint32_t* D,
                         uint32_t* X, int64_t ntiles, hipStream_t s) {
-  tiles_kernel<MODEL, DT><<<dim3((unsigned)ntiles), dim3(256), 0, s>>>(A, B, C, D, X);
+  // a grid-stride loop: 8 workgroups per CU keep every CU busy and give each
+  // workgroup several tiles to overlap its loads with
+  const int64_t grid = ntiles < 2048 ? ntiles : 2048;
+  tilek::tiles_fast_kernel<MODEL, DT>
+      <<<dim3((unsigned)grid), dim3(256), 0, s>>>(A, B, C, D, X, ntiles);
   return hipGetLastError();
 }
 

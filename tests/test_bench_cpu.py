@@ -34,3 +34,13 @@ def test_default_metric_names_the_fp16_ampere_gemm():
     model, _, dt, _, _, _, _ = bench.WORKLOADS[bench.DEFAULT_WORKLOAD]
     assert (f"bit-exact emulated MACs/s, 4096³ {dt.upper()} {model.capitalize()} model; "
             f"% of VALU peak") == "bit-exact emulated MACs/s, 4096³ FP16 Ampere model; % of VALU peak"
+
+
+def test_every_tile_workload_has_a_stored_digest():
+    from bit_exact_matrix_amd import inputs
+    dig = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))
+    for name, (model, mid, dt, did, (gen, gargs), data, key) in bench.TILE_WORKLOADS.items():
+        rec = dig[key]
+        assert rec["model"] == model and rec["dtype"] == dt
+        assert rec["shape"][0] == gargs[1]
+        assert callable(getattr(inputs, gen))
