@@ -126,6 +126,24 @@ def profile_record(name, kernel_hash):
     return rec
 
 
+def cpu_model():
+    """The host CPU's model name (for the oracle baseline), if it can be read."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def launch_stats(launch_ms):
+    n = len(launch_ms)
+    mean = sum(launch_ms) / n
+    std = (sum((x - mean) ** 2 for x in launch_ms) / (n - 1)) ** 0.5 if n > 1 else 0.0
+    return round(min(launch_ms), 4), round(std, 4)
+
+
 def kernel_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "bit_exact_matrix_amd", "csrc")
@@ -195,7 +213,7 @@ def bench_tiles(args):
         Dr, Xr = oracle.tiles(model, dtname, A[:m], B[:m], C[:m], nthreads=nth)
         cs = time.perf_counter() - t
         cpu = {"value": round(m * 4096 / cs, 1), "unit": "MAC/s", "cores": nth,
-               "kind": "oracle", "seconds": round(cs, 2),
+               "kind": "oracle", "cpu_model": cpu_model(), "seconds": round(cs, 2),
                "sample": f"tiles 0..{m - 1} of the batch",
                "sample_matches_gpu": bool(np.array_equal(Dr, D[:m]) and np.array_equal(Xr, X[:m]))}
     out = {
@@ -213,7 +231,8 @@ def bench_tiles(args):
                      "frac": round(achieved / VALU_PEAK_OPS, 4), "traffic": None,
                      "alg_slots_per_mac": ALG_SLOTS_PER_MAC[model],
                      "launch_ms_mean": round(1e3 * avg_s, 4),
-                     "launch_ms_min": round(min(launch_ms), 4)},
+                     "launch_ms_min": launch_stats(launch_ms)[0],
+                     "launch_ms_std": launch_stats(launch_ms)[1]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -355,7 +374,8 @@ def main():
                 "traffic": hbm["bytes_per_launch"] if hbm else None,
                 "alg_slots_per_mac": alg,
                 "launch_ms_mean": round(1e3 * avg_launch_s, 4),
-                "launch_ms_min": round(min(launch_ms), 4)}
+                "launch_ms_min": launch_stats(launch_ms)[0],
+                "launch_ms_std": launch_stats(launch_ms)[1]}
     if valu:
         # executed VALU lane operations (rocprofv3 SQ_INSTS_VALU x 64 for this
         # kernel source) over the live launch time: the VALU share of peak
@@ -383,7 +403,7 @@ def main():
         Dr, Xr = rows_of(rows)
         cs = time.perf_counter() - t
         cpu = {"value": round(rows * N * K / cs, 1), "unit": "MAC/s", "cores": nth,
-               "kind": "oracle", "seconds": round(cs, 2),
+               "kind": "oracle", "cpu_model": cpu_model(), "seconds": round(cs, 2),
                "sample": f"rows 0..{rows - 1} of D ({rows}x{N}x{K} MACs) of the same GEMM",
                "sample_matches_gpu": bool(np.array_equal(Dr, D[:rows])
                                           and (args.verify or np.array_equal(Xr, X[:rows])))}

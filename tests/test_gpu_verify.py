@@ -116,3 +116,18 @@ def test_verify_full_size(torch_dev, orc, name):
         report, X = mm.verify(model, dt, tA, tB, tC, to_dev(torch_dev, claimed), row_diff=True)
         assert mm.mismatches(report) == want[:2]
         assert np.array_equal(to_host_bits(X), want[2])
+
+
+def test_verify_xor_blind_spot(torch_dev, orc):
+    """The same flip in two elements of one row: the row word cancels to 0,
+    the count and first index still report both."""
+    M, N, K = 20, 40, 32
+    A, B, C = _gen("normal", "ampere", "fp16", M, N, K, 6200)
+    D, _ = orc.gemm("ampere", "fp16", A, B, C, xorsum=False)
+    claimed = D.copy()
+    claimed[5, 3] ^= np.uint32(0x100)
+    claimed[5, 30] ^= np.uint32(0x100)
+    claimed[9, 0] ^= np.uint32(0x80000000)
+    count, first, rows = run_verify(torch_dev, "ampere", "fp16", A, B, C, claimed)
+    assert (count, first) == (3, 5 * N + 3)
+    assert rows[5] == 0 and rows[9] == 0x80000000 and np.count_nonzero(rows) == 1

@@ -82,3 +82,18 @@ def test_compare_empty():
     D = np.zeros((3, 0), np.uint32)
     assert compare(D, D)[:2] == (0, None)
     assert compare(D, D)[2].tolist() == [0, 0, 0]
+
+
+def test_row_words_have_the_xor_blind_spot_and_the_count_does_not():
+    """One flipped bit changes exactly its row's word; the same flip in two
+    elements of one row cancels in that row's word, while the mismatch
+    count still sees both (the fingerprint's blind spot, documented)."""
+    from oracle import compare
+    D = (np.arange(12, dtype=np.uint32) + 0x3F800000).reshape(3, 4)
+    claimed = D.copy()
+    claimed[1, 0] ^= 0x10
+    claimed[1, 3] ^= 0x10
+    claimed[2, 2] ^= 0x4
+    count, first, rows = compare(D, claimed)
+    assert (count, first) == (3, 4)
+    assert rows.tolist() == [0, 0, 0x4]
