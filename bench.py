@@ -407,6 +407,22 @@ def main():
                "sample": f"rows 0..{rows - 1} of D ({rows}x{N}x{K} MACs) of the same GEMM",
                "sample_matches_gpu": bool(np.array_equal(Dr, D[:rows])
                                           and (args.verify or np.array_equal(Xr, X[:rows])))}
+        if args.splits == 1:
+            # one thread on a 256-column slice: the oracle's rate per core
+            Bs = np.ascontiguousarray(B[:, :256])
+            Cs = np.ascontiguousarray(C[:, :256])
+            t = time.perf_counter()
+            oracle.gemm_rows(model, dtname, A, Bs, Cs, 0, 4, nthreads=1)
+            per_row = (time.perf_counter() - t) / 4
+            r1 = int(max(4, min(256, args.cpu_seconds / 3 / max(per_row, 1e-9))))
+            t = time.perf_counter()
+            Dp, _ = oracle.gemm_rows(model, dtname, A, Bs, Cs, 0, r1, nthreads=1)
+            c1 = time.perf_counter() - t
+            cpu["per_core"] = {
+                "value": round(r1 * 256 * K / c1, 1), "unit": "MAC/s", "threads": 1,
+                "seconds": round(c1, 2),
+                "sample": f"rows 0..{r1 - 1}, columns 0..255 of D ({r1}x256x{K} MACs)",
+                "sample_matches_gpu": bool(np.array_equal(Dp, D[:r1, :256]))}
 
     out = {
         "metric": (f"bit-exact {'audit-compare' if args.verify else 'emulated'} MACs/s, "

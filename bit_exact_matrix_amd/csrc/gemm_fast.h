@@ -280,18 +280,18 @@ __device__ __forceinline__ void fetch(const void* A, const void* B, int64_t M, i
   }
 }
 
-// Pre-pass: build one operand's images once per GEMM (workspace layout
-// [block][step][OpImage]), so the GEMM kernel only copies them into LDS.
-// One 64-lane workgroup per (step, block); lane r owns row r of an A block
-// (IS_B false) or column r of a B block (IS_B true).
+// Pre-pass: build one operand's images of steps [t0, t0 + gridDim.x) (workspace
+// layout [block][step - t0][OpImage]), so the GEMM kernel only copies them
+// into LDS.  One 64-lane workgroup per (step, block); lane r owns row r of an
+// A block (IS_B false) or column r of a B block (IS_B true).
 template <int MODEL, int DT, bool IS_B>
 __global__ __launch_bounds__(64) void unpack_kernel(const void* __restrict__ src, int64_t limit,
-                                                    int64_t K, int64_t N, int64_t nsteps,
+                                                    int64_t K, int64_t N, int64_t t0,
                                                     uint32_t* __restrict__ ws) {
-  const int64_t s = blockIdx.x, blk = blockIdx.y;
+  const int64_t s = t0 + blockIdx.x, blk = blockIdx.y;
   const int r = threadIdx.x;
   const int64_t idx = blk * 64 + r;
-  OpImage* img = (OpImage*)(ws + (blk * nsteps + s) * IMG_WORDS);
+  OpImage* img = (OpImage*)(ws + (blk * gridDim.x + blockIdx.x) * IMG_WORDS);
   uint32_t codes[16];
   // an A row segment is 16 consecutive codes: two (or, for E4M3, one)
   // 16-byte loads when the row start is 16-byte aligned
@@ -618,24 +618,25 @@ template <int MODEL, bool DMA>
 constexpr int kWavesPerSimd = DMA ? 3 : 2;
 
 // DMA = true: the operand images come from the pre-pass workspace (ws_a,
-// ws_b) by direct global->LDS copies; DMA = false: the kernel builds them
-// from the raw codes (no workspace).  The kernel chains the ns steps that
-// start at step s0 (all K/16 of them for a plain GEMM, one run of a split-K
-// schedule otherwise).  The K loop is unrolled twice so that the
+// ws_b, holding steps [i0, i0 + istride) of every block) by direct
+// global->LDS copies; DMA = false: the kernel builds them from the raw codes
+// (no workspace).  The kernel chains the ns steps that start at step s0 (all
+// K/16 of them for a plain GEMM; one run of a split-K schedule, or one chunk
+// of steps when the workspace holds fewer than all of them, otherwise).  The K loop is unrolled twice so that the
 // accumulator state alternates between two register sets instead of being
 // copied back every step.
 template <int MODEL, int DT, bool DMA>
 __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
     int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns,
-    const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b) {
+    const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b, int64_t i0,
+    int64_t istride) {
   __shared__ Stage stage[2];
   const int t = threadIdx.x;
   const int ty = t >> 4, tx = t & 15;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int64_t bm = (int64_t)blockIdx.y * BM, bn = (int64_t)blockIdx.x * BN;
-  const int64_t nsteps = ns;           // steps chained here
-  const int64_t total = K / 16;        // steps of the whole GEMM (image stride)
+  const int64_t nsteps = ns;  // steps chained here
 
   int X[4][4], Xn[4][4];
   uint32_t NE[2][4], NEn[2][4];
@@ -654,9 +655,9 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
     }
 
   const uint32_t* img_a =
-      DMA ? ws_a + ((int64_t)blockIdx.y * total + s0) * IMG_WORDS : nullptr;
+      DMA ? ws_a + ((int64_t)blockIdx.y * istride + (s0 - i0)) * IMG_WORDS : nullptr;
   const uint32_t* img_b =
-      DMA ? ws_b + ((int64_t)blockIdx.x * total + s0) * IMG_WORDS : nullptr;
+      DMA ? ws_b + ((int64_t)blockIdx.x * istride + (s0 - i0)) * IMG_WORDS : nullptr;
   uint32_t ca[4], cb[4];
   // fill of stage s (local step s, absolute step s0 + s): start it (before
   // the previous step's compute), end it
@@ -765,38 +766,72 @@ inline int64_t gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (mb + nb) * (K / 16) * (int64_t)sizeof(fastk::OpImage);
 }
 
-// ws: NULL for the in-kernel image build, else gemm_fast_workspace_bytes() bytes.
+// ws: NULL for the in-kernel image build, else a workspace that holds the
+// images of ws_steps steps of every A block and every B block
+// (gemm_fast_workspace_bytes(M, N, 16 * ws_steps) bytes).
 // splits > 1 (a divisor of K/16): the split-K schedule.  Run r chains steps
 // [r*T/splits, (r+1)*T/splits) of the T = K/16 steps, from C for r = 0 and
 // from +0 otherwise; the runs are launched in order and each later one adds
 // its partial result into D (fp32_add_rne), so that D = ((P0 + P1) + P2)...
 // The xorsum, if any, is taken by the last run, over the final D.
+// A workspace too small for all T steps is filled once per run, or, when it
+// cannot hold a whole run, run 0 of an emulating call is cut into chunks of
+// ws_steps steps, each restarting from the D that the previous chunk wrote:
+// every step's result is an FP32 value, so the chain through D is the same
+// chain.  What remains (a later run, the audit compare) builds its images in
+// LDS.
 template <int MODEL, int DT>
 inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, const Sink& out,
-                             int64_t M, int64_t N, int64_t K, void* ws, hipStream_t s,
-                             int64_t splits = 1) {
+                             int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_steps,
+                             hipStream_t s, int64_t splits = 1) {
   const int64_t mb = (M + fastk::BM - 1) / fastk::BM, nb = (N + fastk::BN - 1) / fastk::BN;
   const int64_t nsteps = K / 16, per = nsteps / splits;
   const dim3 grid((unsigned)nb, (unsigned)mb);
+  if (!ws) ws_steps = 0;
   uint32_t* ws_a = (uint32_t*)ws;
-  uint32_t* ws_b = ws ? ws_a + mb * nsteps * fastk::IMG_WORDS : nullptr;
-  if (ws) {
+  uint32_t* ws_b = ws ? ws_a + mb * ws_steps * fastk::IMG_WORDS : nullptr;
+  // the images of steps [t0, t0 + n), n <= ws_steps
+  auto prepass = [&](int64_t t0, int64_t n) {
     fastk::unpack_kernel<MODEL, DT, false>
-        <<<dim3((unsigned)nsteps, (unsigned)mb), dim3(64), 0, s>>>(A, M, K, N, nsteps, ws_a);
+        <<<dim3((unsigned)n, (unsigned)mb), dim3(64), 0, s>>>(A, M, K, N, t0, ws_a);
     fastk::unpack_kernel<MODEL, DT, true>
-        <<<dim3((unsigned)nsteps, (unsigned)nb), dim3(64), 0, s>>>(B, N, K, N, nsteps, ws_b);
-  }
+        <<<dim3((unsigned)n, (unsigned)nb), dim3(64), 0, s>>>(B, N, K, N, t0, ws_b);
+  };
+  // steps [t0, t0 + n) from c into o, with the images of steps [i0, i0 + istride)
+  // in the workspace (istride = 0: built in LDS)
+  auto chain = [&](const uint32_t* c, const Sink& o, int64_t t0, int64_t n, int64_t i0,
+                   int64_t istride) {
+    if (istride > 0) {
+      fastk::gemm_fast_kernel<MODEL, DT, true><<<grid, dim3(fastk::NT), 0, s>>>(
+          A, B, c, o, M, N, K, t0, n, ws_a, ws_b, i0, istride);
+    } else {
+      fastk::gemm_fast_kernel<MODEL, DT, false><<<grid, dim3(fastk::NT), 0, s>>>(
+          A, B, c, o, M, N, K, t0, n, nullptr, nullptr, 0, 0);
+    }
+  };
+  const bool whole = ws_steps >= nsteps;
+  if (whole) prepass(0, nsteps);
   for (int64_t r = 0; r < splits; ++r) {
     Sink o = out;
     o.accumulate = r > 0;
     if (r + 1 < splits) o.xorsum = nullptr;
     const uint32_t* c = r == 0 ? C : nullptr;
-    if (ws) {
-      fastk::gemm_fast_kernel<MODEL, DT, true>
-          <<<grid, dim3(fastk::NT), 0, s>>>(A, B, c, o, M, N, K, r * per, per, ws_a, ws_b);
+    const int64_t t0 = r * per;
+    if (whole) {
+      chain(c, o, t0, per, 0, nsteps);
+    } else if (ws_steps >= per) {
+      prepass(t0, per);
+      chain(c, o, t0, per, t0, per);
+    } else if (r > 0 || !out.D || ws_steps == 0) {
+      chain(c, o, t0, per, 0, 0);
     } else {
-      fastk::gemm_fast_kernel<MODEL, DT, false>
-          <<<grid, dim3(fastk::NT), 0, s>>>(A, B, c, o, M, N, K, r * per, per, nullptr, nullptr);
+      for (int64_t u = 0; u < per; u += ws_steps) {
+        const int64_t n = per - u < ws_steps ? per - u : ws_steps;
+        Sink oc = o;
+        if (u + n < per) oc.xorsum = nullptr;
+        prepass(t0 + u, n);
+        chain(u == 0 ? c : out.D, oc, t0 + u, n, t0 + u, n);
+      }
     }
   }
 }

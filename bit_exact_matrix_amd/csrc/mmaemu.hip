@@ -151,16 +151,32 @@ bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return true;
 }
 
+// The largest operand-image workspace one call takes: 1 GiB, or the byte
+// count in MMAEMU_WORKSPACE_MAX_BYTES; 0 there, or MMAEMU_NO_WORKSPACE set,
+// turns the workspace off.  Read on every call.
+constexpr int64_t kDefaultWorkspaceCap = int64_t(1) << 30;
+
+int64_t workspace_cap() {
+  if (getenv("MMAEMU_NO_WORKSPACE")) return 0;
+  const char* v = getenv("MMAEMU_WORKSPACE_MAX_BYTES");
+  if (v && *v) {
+    char* end = nullptr;
+    const long long x = strtoll(v, &end, 10);
+    if (end && *end == '\0' && x >= 0) return (int64_t)x;
+  }
+  return kDefaultWorkspaceCap;
+}
+
 // Stream-ordered workspace for the operand pre-pass, from one memory pool
-// per device that keeps freed memory cached (release threshold = max), so
-// repeated calls do not go back to the driver.  A failed allocation is not
-// an error: the caller falls back to the kernel that unpacks in place.
+// per device.  The pool keeps up to the default cap of freed memory cached
+// (its release threshold), so repeated calls do not go back to the driver,
+// and returns the rest at the next synchronisation.  A failed allocation is
+// not an error: the caller falls back to the kernel that unpacks in place.
 constexpr int kMaxDevices = 64;
 hipMemPool_t g_pool[kMaxDevices];
 std::once_flag g_pool_once[kMaxDevices];
 
 void* workspace_alloc(int64_t bytes, hipStream_t s) {
-  if (getenv("MMAEMU_NO_WORKSPACE")) return nullptr;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
     (void)hipGetLastError();
@@ -173,7 +189,7 @@ void* workspace_alloc(int64_t bytes, hipStream_t s) {
     props.location.type = hipMemLocationTypeDevice;
     props.location.id = dev;
     if (hipMemPoolCreate(&g_pool[dev], &props) == hipSuccess) {
-      uint64_t keep = UINT64_MAX;
+      uint64_t keep = (uint64_t)kDefaultWorkspaceCap;
       (void)hipMemPoolSetAttribute(g_pool[dev], hipMemPoolAttrReleaseThreshold, &keep);
     } else {
       g_pool[dev] = nullptr;
@@ -199,8 +215,15 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
   if (out.report) init_report_kernel<<<dim3(1), dim3(64), 0, s>>>(out.report);
   if (M == 0 || N == 0) return hipGetLastError();
   if (gemm_fast_supported(M, N, K)) {
-    void* ws = workspace_alloc(gemm_fast_workspace_bytes(M, N, K), s);
-    gemm_fast_launch<MODEL, DT>(A, B, C, out, M, N, K, ws, s, splits);
+    // as many steps of operand images as the cap allows: all K/16, else one
+    // split-K run's worth, else fewer (chunks)
+    const int64_t nsteps = K / 16, per = nsteps / splits;
+    const int64_t step_bytes = gemm_fast_workspace_bytes(M, N, 16);
+    int64_t ws_steps = workspace_cap() / step_bytes;
+    if (ws_steps > nsteps) ws_steps = nsteps;
+    if (ws_steps < nsteps && ws_steps > per) ws_steps = per;
+    void* ws = ws_steps > 0 ? workspace_alloc(ws_steps * step_bytes, s) : nullptr;
+    gemm_fast_launch<MODEL, DT>(A, B, C, out, M, N, K, ws, ws_steps, s, splits);
     if (ws) {
       // the free is ordered after the kernels; it is issued whatever the
       // launches returned, so that a failed call does not hold the memory

@@ -36,11 +36,19 @@
  * MEMORY AND LAYOUT
  *   Every pointer is a DEVICE pointer on the current HIP device, owned by
  *   the caller.  mma_emulate_gemm and mma_emulate_gemm_async stage the
- *   operands through a temporary workspace of
- *   12 KiB x (ceil(M/64) + ceil(N/64)) x K/16 bytes (384 MiB at 4096^3),
+ *   operands through a temporary workspace of operand images, 12 KiB per
+ *   K-step for each 64-row block of A and each 64-column block of B: all
+ *   K/16 steps take 12 KiB x (ceil(M/64) + ceil(N/64)) x K/16 bytes (384 MiB
+ *   at 4096^3).  One call takes at most 1 GiB of it, or the byte count in
+ *   the environment variable MMAEMU_WORKSPACE_MAX_BYTES (read on every
+ *   call).  When the images of all steps do not fit, the call fills the
+ *   workspace once per split-K run, or cuts the chain into runs of steps
+ *   that restart from the D the previous one wrote (exact: every step's
+ *   result is an FP32 value); the results are the same.  The workspace is
  *   allocated and freed in stream order from a per-device memory pool that
- *   the library creates on first use and keeps, with the memory it has
- *   cached, until the process ends.  If that allocation fails, or the
+ *   the library creates on first use and keeps until the process ends,
+ *   with up to 1 GiB of freed memory cached for later calls.  If the
+ *   allocation fails, the cap is below one step's images, or the
  *   environment variable MMAEMU_NO_WORKSPACE is set, the call stages the
  *   operands in LDS instead (same results, slower) and allocates nothing.
  *   mma_emulate_tiles allocates nothing.  No other state is kept between
