@@ -215,8 +215,8 @@ __device__ __forceinline__ void image_b(uint32_t code, uint32_t& val, int& sgn, 
 
 // In-kernel image builder (no workspace): lane (k = t & 15, q = t >> 4)
 // handles A rows 4q..4q+3 and B cols 4q..4q+3 at k.
-template <int MODEL, int DT>
-__device__ __forceinline__ void produce(Stage* st, const uint32_t (&ca)[4],
+template <int MODEL, int DT, typename ST>
+__device__ __forceinline__ void produce(ST* st, const uint32_t (&ca)[4],
                                         const uint32_t (&cb)[4], int t) {
   const int k = t & 15, q = t >> 4;
   uint32_t av[4], ane[4], bv[4], bne[4];
@@ -404,8 +404,8 @@ __device__ __forceinline__ void lds_quad(const T* row, int tx, T (&v)[4]) {
 // of them) for pass 2; otherwise pass 2 recomputes them.
 // Returns S (signed exact group sum on the grid of the group's emax) and
 // mn (= 0x4000 - emax, paired like ne_t) for the pairs it covers.
-template <int NP, bool STORE_ES, bool NT_EMPTY, int QB = 0, int QN = 2>
-__device__ __forceinline__ void group(const Stage* st, int ty, int tx, int p0, int gmask,
+template <int NP, bool STORE_ES, bool NT_EMPTY, int QB = 0, int QN = 2, typename ST>
+__device__ __forceinline__ void group(const ST* st, int ty, int tx, int p0, int gmask,
                                       const uint32_t (&ne_t)[2][4], const int (&X_t)[4][4],
                                       int (&S)[4][4], uint32_t (&mn_out)[2][4]) {
   static_assert(STORE_ES || !NT_EMPTY, "an empty extra term needs the stored exponents");
@@ -532,15 +532,19 @@ __device__ __forceinline__ void normalise2(int S0, int S1, uint32_t mn, int& X0,
 }
 
 // One chained MMA step for the lane's 4x4 outputs: state (X, NE) in,
-// (Xn, NEn) out.  Outputs whose fast result is not trustworthy (a zero
-// result, a result below FP32's normal range, an inf/NaN operand) are redone
-// exactly from the raw codes, for the whole lane tile.
-template <int MODEL, int DT>
-__device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const void* A,
-                                          const void* B, int64_t M, int64_t N, int64_t K,
-                                          int64_t s, const int (&X)[4][4],
-                                          const uint32_t (&NE)[2][4],
-                                          int (&Xn)[4][4], uint32_t (&NEn)[2][4]) {
+// (Xn, NEn) out.  The lane reads rows 4*ty .. 4*ty+3 of the stage's A image
+// and columns 4*tx .. 4*tx+3 of its B image.  A fast result is not
+// trustworthy when it is zero, below FP32's normal range or touched by an
+// inf/NaN operand.  MASK = false: if any output's is not, the whole lane
+// tile is redone exactly from the raw codes, redo(r, c, X, ne) returning the
+// new state of output (r, c) from its previous state.  MASK = true: nothing
+// is redone; bit 4r + c of bad is set for each such output (r, c), whose
+// (Xn, NEn) must then be ignored.
+template <int MODEL, int DT, bool MASK = false, typename ST, typename REDO>
+__device__ __forceinline__ void tile_step(const ST* st, int ty, int tx, const int (&X)[4][4],
+                                          const uint32_t (&NE)[2][4], int (&Xn)[4][4],
+                                          uint32_t (&NEn)[2][4], REDO&& redo,
+                                          uint32_t* bad = nullptr) {
   constexpr int F = Model<MODEL>::F;
   int S[4][4];
   uint32_t mn[2][4];
@@ -553,8 +557,13 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
       normalise2<F - 23, F>(S[2 * q][c], S[2 * q + 1][c], mn[q][c], Xn[2 * q][c],
                             Xn[2 * q + 1][c], NEn[q][c]);
       const uint32_t ne = NEn[q][c];
-      rng = __builtin_elementwise_max(
-          rng, as2(ne) - u16x2{(unsigned short)NE_OK_LO, (unsigned short)NE_OK_LO});
+      const u16x2 off = as2(ne) - u16x2{(unsigned short)NE_OK_LO, (unsigned short)NE_OK_LO};
+      if constexpr (MASK) {
+        *bad |= (uint32_t)(off.x > NE_OK_SPAN) << (8 * q + c);
+        *bad |= (uint32_t)(off.y > NE_OK_SPAN) << (8 * q + 4 + c);
+      } else {
+        rng = __builtin_elementwise_max(rng, off);
+      }
       // FP32 overflow (L >= 128): the state becomes inf.  FP16 and E4M3
       // products stay below 2^33, so L = 128 already dominates them and a
       // max suffices; BF16 products reach 2^256 and need E = 1024.
@@ -592,16 +601,14 @@ __device__ __forceinline__ void tile_step(const Stage* st, int ty, int tx, const
     group<8, true, false, 1, 1>(st, ty, tx, 0, 0, NE, X, S, mn);
     finish(1);
   }
-  if ((rng.x > NE_OK_SPAN) | (rng.y > NE_OK_SPAN)) {
+  if (!MASK && ((rng.x > NE_OK_SPAN) | (rng.y > NE_OK_SPAN))) {
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         // recompute the whole 4x4 tile from the previous state
-        const uint2 v0 = slow_step<MODEL, DT>(A, B, M, N, K, s, 2 * q, c, X[2 * q][c],
-                                              NE[q][c] & 0xFFFFu);
-        const uint2 v1 = slow_step<MODEL, DT>(A, B, M, N, K, s, 2 * q + 1, c, X[2 * q + 1][c],
-                                              NE[q][c] >> 16);
+        const uint2 v0 = redo(2 * q, c, X[2 * q][c], NE[q][c] & 0xFFFFu);
+        const uint2 v1 = redo(2 * q + 1, c, X[2 * q + 1][c], NE[q][c] >> 16);
         Xn[2 * q][c] = (int)v0.x;
         Xn[2 * q + 1][c] = (int)v1.x;
         NEn[q][c] = v0.y | v1.y << 16;
@@ -681,9 +688,15 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
   }
   __syncthreads();
 
+  // the exact recompute of output (r, c) of the lane's tile at step ks
+  auto redo_at = [&](int64_t ks) {
+    return [=](int r, int c, int x, uint32_t ne) {
+      return slow_step<MODEL, DT>(A, B, M, N, K, ks, r, c, x, ne);
+    };
+  };
   for (int64_t s = 0; s < nsteps; s += 2) {
     if (s + 1 < nsteps) begin_fill(s + 1);
-    tile_step<MODEL, DT>(&stage[s & 1], ty, tx, A, B, M, N, K, s0 + s, X, NE, Xn, NEn);
+    tile_step<MODEL, DT>(&stage[s & 1], ty, tx, X, NE, Xn, NEn, redo_at(s0 + s));
     if (s + 1 < nsteps) end_fill(s + 1);
     __syncthreads();
     if (s + 1 >= nsteps) {
@@ -698,8 +711,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
       break;
     }
     if (s + 2 < nsteps) begin_fill(s + 2);
-    tile_step<MODEL, DT>(&stage[(s + 1) & 1], ty, tx, A, B, M, N, K, s0 + s + 1, Xn, NEn, X,
-                         NE);
+    tile_step<MODEL, DT>(&stage[(s + 1) & 1], ty, tx, Xn, NEn, X, NE, redo_at(s0 + s + 1));
     if (s + 2 < nsteps) end_fill(s + 2);
     __syncthreads();
   }
