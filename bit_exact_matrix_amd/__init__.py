@@ -121,12 +121,14 @@ def _enum(v, table):
     return table[v.lower()] if isinstance(v, str) else int(v)
 
 
-def _dev_ptr(t, what, nbytes_elem=None):
+def _dev_ptr(t, what, nbytes_elem=None, device=None):
     import torch
     if t is None:
         return None
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TypeError(f"{what} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, the call runs on {device}")
     if not t.is_contiguous():
         raise ValueError(f"{what} must be contiguous")
     if nbytes_elem is not None and t.element_size() != nbytes_elem:
@@ -139,10 +141,29 @@ def _check_shape(t, shape, what):
         raise ValueError(f"{what} must have shape {tuple(shape)}, got {tuple(t.shape)}")
 
 
-def _stream_handle(stream):
+def _launch(A, stream):
+    """The device of A (every operand must be there) and the launch stream:
+    the given one, else that device's current stream.  The wrappers make
+    the device current and allocate their outputs under the launch stream,
+    so that torch's allocator ties them to the stream that writes them."""
     import torch
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream
+    if not isinstance(A, torch.Tensor) or not A.is_cuda:
+        raise TypeError("A must be a device tensor")
+    dev = A.device
+    s = stream if stream is not None else torch.cuda.current_stream(dev)
+    if s.device != dev:
+        raise ValueError(f"the stream is on {s.device}, the operands on {dev}")
+    return dev, s
+
+
+def _matrix_shapes(A, B):
+    if A.dim() != 2 or B.dim() != 2:
+        raise ValueError("A and B must be matrices")
+    M, K = A.shape
+    K2, N = B.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    return M, N, K
 
 
 def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None, splits=1):
@@ -157,19 +178,18 @@ def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None, splits=1
     import torch
     m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
     esz = 1 if d == FP8_E4M3 else 2
-    M, K = A.shape
-    K2, N = B.shape
-    if K != K2:
-        raise ValueError("inner dimensions differ")
+    dev, s = _launch(A, stream)
+    M, N, K = _matrix_shapes(A, B)
     _check_shape(C, (M, N), "C")
     _check_shape(D, (M, N), "D")
-    if D is None:
-        D = torch.empty((M, N), dtype=torch.float32, device=A.device)
-    X = torch.empty(M, dtype=torch.int32, device=A.device) if xorsum else None
-    rc = mma_emulate_gemm_splitk_async(m, d, _dev_ptr(A, "A", esz), _dev_ptr(B, "B", esz),
-                                       _dev_ptr(C, "C", 4), _dev_ptr(D, "D", 4), M, N, K,
-                                       int(splits), _dev_ptr(X, "xorsum"),
-                                       _stream_handle(stream))
+    with torch.cuda.device(dev), torch.cuda.stream(s):
+        if D is None:
+            D = torch.empty((M, N), dtype=torch.float32, device=dev)
+        X = torch.empty(M, dtype=torch.int32, device=dev) if xorsum else None
+        rc = mma_emulate_gemm_splitk_async(
+            m, d, _dev_ptr(A, "A", esz, dev), _dev_ptr(B, "B", esz, dev),
+            _dev_ptr(C, "C", 4, dev), _dev_ptr(D, "D", 4, dev), M, N, K, int(splits),
+            _dev_ptr(X, "xorsum", None, dev), s.cuda_stream)
     if rc != 0:
         raise MmaEmuError(rc, "mma_emulate_gemm_splitk_async")
     return D, X
@@ -188,18 +208,18 @@ def verify(model, dtype, A, B, C, D_claimed, row_diff=False, stream=None):
     import torch
     m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
     esz = 1 if d == FP8_E4M3 else 2
-    M, K = A.shape
-    K2, N = B.shape
-    if K != K2:
-        raise ValueError("inner dimensions differ")
+    dev, s = _launch(A, stream)
+    M, N, K = _matrix_shapes(A, B)
     _check_shape(C, (M, N), "C")
     _check_shape(D_claimed, (M, N), "D_claimed")
-    report = torch.empty(2, dtype=torch.int64, device=A.device)
-    X = torch.empty(M, dtype=torch.int32, device=A.device) if row_diff else None
-    rc = mma_verify_gemm_async(m, d, _dev_ptr(A, "A", esz), _dev_ptr(B, "B", esz),
-                               _dev_ptr(C, "C", 4), _dev_ptr(D_claimed, "D_claimed", 4),
-                               M, N, K, _dev_ptr(report, "report"), _dev_ptr(X, "row_diff"),
-                               _stream_handle(stream))
+    with torch.cuda.device(dev), torch.cuda.stream(s):
+        report = torch.empty(2, dtype=torch.int64, device=dev)
+        X = torch.empty(M, dtype=torch.int32, device=dev) if row_diff else None
+        rc = mma_verify_gemm_async(
+            m, d, _dev_ptr(A, "A", esz, dev), _dev_ptr(B, "B", esz, dev),
+            _dev_ptr(C, "C", 4, dev), _dev_ptr(D_claimed, "D_claimed", 4, dev), M, N, K,
+            _dev_ptr(report, "report", None, dev), _dev_ptr(X, "row_diff", None, dev),
+            s.cuda_stream)
     if rc != 0:
         raise MmaEmuError(rc, "mma_verify_gemm_async")
     return report, X
@@ -216,17 +236,19 @@ def tiles(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
     import torch
     m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
     esz = 1 if d == FP8_E4M3 else 2
-    n = A.shape[0]
+    dev, s = _launch(A, stream)
+    n = A.shape[0] if A.dim() == 3 else -1
     if tuple(A.shape) != (n, 16, 16) or tuple(B.shape) != (n, 16, 16):
         raise ValueError("A and B must be [ntiles, 16, 16]")
     _check_shape(C, (n, 16, 16), "C")
     _check_shape(D, (n, 16, 16), "D")
-    if D is None:
-        D = torch.empty((n, 16, 16), dtype=torch.float32, device=A.device)
-    X = torch.empty(n, dtype=torch.int32, device=A.device) if xorsum else None
-    rc = mma_emulate_tiles(m, d, _dev_ptr(A, "A", esz), _dev_ptr(B, "B", esz),
-                           _dev_ptr(C, "C", 4), _dev_ptr(D, "D", 4), n,
-                           _dev_ptr(X, "xorsum"), _stream_handle(stream))
+    with torch.cuda.device(dev), torch.cuda.stream(s):
+        if D is None:
+            D = torch.empty((n, 16, 16), dtype=torch.float32, device=dev)
+        X = torch.empty(n, dtype=torch.int32, device=dev) if xorsum else None
+        rc = mma_emulate_tiles(m, d, _dev_ptr(A, "A", esz, dev), _dev_ptr(B, "B", esz, dev),
+                               _dev_ptr(C, "C", 4, dev), _dev_ptr(D, "D", 4, dev), n,
+                               _dev_ptr(X, "xorsum", None, dev), s.cuda_stream)
     if rc != 0:
         raise MmaEmuError(rc, "mma_emulate_tiles")
     return D, X

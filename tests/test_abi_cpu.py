@@ -104,3 +104,21 @@ R = 0x60000000  # fake report address
 def test_verify_argument_errors(args, code):
     assert mm.mma_verify_gemm_async(*args, None) == code
     assert mm.mma_verify_gemm(*args) == code
+
+
+def test_torch_wrappers_reject_host_tensors_before_any_launch():
+    """The torch wrappers check their operands on the host: a CPU tensor, a
+    non-matrix or mismatched inner dimensions raise before the library is
+    called."""
+    import torch
+    a = torch.zeros((16, 16), dtype=torch.int16)
+    with pytest.raises(TypeError, match="device tensor"):
+        mm.gemm("ampere", "fp16", a, a)
+    with pytest.raises(TypeError, match="device tensor"):
+        mm.verify("hopper", "bf16", a, a, None, torch.zeros((16, 16)))
+    with pytest.raises(TypeError, match="device tensor"):
+        mm.tiles("ampere", "fp16", a.reshape(1, 16, 16), a.reshape(1, 16, 16))
+    with pytest.raises(ValueError, match="matrices|inner"):
+        mm._matrix_shapes(a.reshape(1, 16, 16), a)
+    with pytest.raises(ValueError, match="inner dimensions"):
+        mm._matrix_shapes(torch.zeros((16, 32)), torch.zeros((16, 16)))
