@@ -81,6 +81,12 @@ __global__ void init_report_kernel(unsigned long long* report) {
 // ------------------------------------------------------------- plumbing
 thread_local char g_hip_error[256] = "no HIP error recorded";
 
+// Launch failures are read back with hipGetLastError, which also returns
+// an error that an earlier, unrelated HIP call left pending in this thread.
+// Such an error predates the call: it is cleared before the first launch
+// so that it is not reported as this call's.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
 int hip_fail(hipError_t e, const char* where) {
   snprintf(g_hip_error, sizeof g_hip_error, "HIP error in %s: %s", where,
            hipGetErrorString(e));
@@ -303,6 +309,7 @@ int gemm_impl(int model, int dtype, const void* A, const void* B, const float* C
                    g.cd ? C : nullptr, g.cd ? D : nullptr, g.cd, xorsum, xorsum ? M * 4 : 0);
   if (rc) return rc;
   const Sink out{(uint32_t*)D, xorsum, nullptr, nullptr, 0};
+  clear_stale_hip_error();
   const hipError_t e = MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C,
                                        out, M, N, K, s, splits);
   if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm launch");
@@ -326,6 +333,7 @@ int verify_impl(int model, int dtype, const void* A, const void* B, const float*
   if (rc) return rc;
   const Sink out{nullptr, row_diff, (const uint32_t*)D_claimed, (unsigned long long*)report,
                  0};
+  clear_stale_hip_error();
   const hipError_t e =
       MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C, out, M, N, K, s);
   if (e != hipSuccess) return hip_fail(e, "mma_verify_gemm launch");
@@ -398,6 +406,7 @@ int mma_emulate_tiles(int model, int dtype, const void* A, const void* B, const 
   rc = check_alias(A, ntiles * 256 * esz, B, ntiles * 256 * esz, C, D, ntiles * 1024,
                    xorsum_out, xorsum_out ? ntiles * 4 : 0);
   if (rc) return rc;
+  clear_stale_hip_error();
   const hipError_t e =
       MMAEMU_DISPATCH(model, dtype, launch_tiles, A, B, (const uint32_t*)C, (uint32_t*)D,
                       xorsum_out, ntiles, (hipStream_t)hip_stream);

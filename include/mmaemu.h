@@ -66,7 +66,10 @@
  *   Argument errors are reported before anything is enqueued and leave all
  *   buffers untouched.  A failed launch returns MMAEMU_ERR_HIP; the text of
  *   the HIP error is available from mma_emulate_strerror(MMAEMU_ERR_HIP)
- *   on the same thread.  No C++ exception crosses this interface.
+ *   on the same thread.  A HIP error that an earlier, unrelated call left
+ *   pending in the calling thread (hipGetLastError) is cleared before the
+ *   first launch and not reported.  No C++ exception crosses this
+ *   interface.
  *
  * DETERMINISM
  *   The same inputs give the same D and xorsum bits on every call, stream
