@@ -282,7 +282,7 @@ def _random_dot_inputs(rng, dtype, n, adversarial):
 @pytest.mark.parametrize("adversarial", [False, True])
 def test_oracle_matches_rational_model(orc, model, dtype, adversarial):
     rng = np.random.default_rng(100 + 10 * model + dtype + (5 if adversarial else 0))
-    n = 6000
+    n = 10000   # 10 cases: 100,000 single steps in all
     a, b, c = _random_dot_inputs(rng, dtype, n, adversarial)
     got = orc.dots(model, dtype, a, b, c)
     for r in range(n):
