@@ -73,3 +73,39 @@ def test_unaligned_operands(torch_dev, orc, model, dt):
     say("tiles unaligned", model, dt)
     D, X = mm.tiles(model, dt, tA, tB, tC, D=tD, xorsum=True)
     _check(torch_dev, model, dt, A, B, C, D, X, orc, f"tiles unaligned {model}/{dt}")
+
+
+@pytest.mark.parametrize("model,dt", COMBOS)
+def test_largest_group_sums(torch_dev, orc, model, dt):
+    """Every significand all ones at one exponent, C a full FP32 significand
+    at the products' exponent, all of one sign (then all negative, then
+    alternating by tile): the largest sums a group forms (the bound that
+    lets the kernel accumulate in 32 bits), in tiles and in a GEMM chain."""
+    torch, dev = torch_dev
+    one = {"fp16": 0x3FFF, "bf16": 0x3FFF, "e4m3": 0x3F}[dt]       # 1.11..1 x 2^0
+    sign = {"fp16": 0x8000, "bf16": 0x8000, "e4m3": 0x80}[dt]
+    code = np.uint8 if dt == "e4m3" else np.uint16
+    n = 8
+    A = np.full((n, 16, 16), one, code)
+    B = np.full((n, 16, 16), one, code)
+    C = np.full((n, 16, 16), 0x3FFFFFFF, np.uint32)                  # 1.11..1 x 2^0
+    A[1::2] |= code(sign)                                             # negative products
+    C[1::2] |= np.uint32(0x80000000)
+    A[2:4] |= code(sign)
+    B[2:4] |= code(sign)                                              # (-)(-): positive
+    C[4:6] |= np.uint32(0x80000000)                                   # C against the products
+    say("largest group sums", model, dt)
+    D, X = mm.tiles(model, dt, to_dev(torch_dev, A), to_dev(torch_dev, B),
+                    to_dev(torch_dev, C), xorsum=True)
+    _check(torch_dev, model, dt, A, B, C, D, X, orc, f"largest sums tiles {model}/{dt}")
+    # the same operands as one 128 x 16 x 128 GEMM chain (eight steps)
+    Ag = A.reshape(128, 16)
+    Bg = np.ascontiguousarray(np.tile(B[0], (8, 8)))
+    Cg = C.reshape(128, 16)[:, :16]
+    Cg = np.ascontiguousarray(np.tile(Cg, (1, 8)))
+    Ag = np.ascontiguousarray(np.tile(Ag, (1, 8)))
+    want, wx = orc.gemm(model, dt, Ag, Bg, Cg)
+    D, X = mm.gemm(model, dt, to_dev(torch_dev, Ag), to_dev(torch_dev, Bg),
+                   to_dev(torch_dev, Cg), xorsum=True)
+    assert_bits_equal(to_host_bits(D), want, f"largest sums gemm {model}/{dt}")
+    assert_bits_equal(to_host_bits(X), wx, f"largest sums gemm xorsum {model}/{dt}")
