@@ -241,8 +241,8 @@ def bench_tiles(args):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the GEMM shards over rows of D with no exchange; see the design notes).",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the GEMM would shard over rows of D, with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
     if args.workload in TILE_WORKLOADS:
