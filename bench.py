@@ -12,8 +12,8 @@ against a claimed D equal to the oracle's.  --splits S times the split-K
 schedule (mma_emulate_gemm_splitk: S runs of K/(16 S) steps, partial
 results added in FP32 round-to-nearest-even).
 
-Prints ONE JSON line.  --gpus above 1 is refused (one GPU per process and
-box; the path shards over rows of D, see the design notes).
+Prints ONE JSON line.  --gpus above 1 is refused: the library runs on one
+GPU (the path would shard over rows of D, with no exchange).
 """
 from __future__ import annotations
 

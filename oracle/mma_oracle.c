@@ -11,7 +11,7 @@
  * quantities are kept in int64 so that no step can overflow.
  *
  * Rules (each cites the page passage it follows; "reading:" marks a choice
- * where the pages are silent, listed again in the design notes):
+ * where the pages are silent):
  *
  *  R1  Formats.  FP16 (10 fraction bits, bias 15), BF16 (7, 127), FP8 E4M3
  *      (3, 7; reading: the OCP "FN" variant -- no infinities, NaN = S.1111.111),
