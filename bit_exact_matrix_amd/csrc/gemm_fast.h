@@ -629,16 +629,25 @@ constexpr int kWavesPerSimd = DMA ? 3 : 2;
 // global->LDS copies; DMA = false: the kernel builds them from the raw codes
 // (no workspace).  The kernel chains the ns steps that start at step s0 (all
 // K/16 of them for a plain GEMM; one run of a split-K schedule, or one chunk
-// of steps when the workspace holds fewer than all of them, otherwise).  The K loop is unrolled twice so that the
-// accumulator state alternates between two register sets instead of being
-// copied back every step.
+// of steps when the workspace holds fewer than all of them, otherwise).
+// With gridDim.z > 1 the z-th slice of the grid chains the ns steps that
+// start at s0 + z*ns instead, from +0 when z > 0, and stores into the D of
+// out moved on by z*zstride words: the runs of a split-K schedule side by
+// side.  The K loop is unrolled twice so that the accumulator state
+// alternates between two register sets instead of being copied back every
+// step.
 template <int MODEL, int DT, bool DMA>
 __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_kernel(
-    const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
-    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns,
+    const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C0, Sink out0,
+    int64_t M, int64_t N, int64_t K, int64_t s00, int64_t ns,
     const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b, int64_t i0,
-    int64_t istride) {
+    int64_t istride, int64_t zstride) {
   __shared__ Stage stage[2];
+  const int64_t z = blockIdx.z;
+  const uint32_t* const C = z ? nullptr : C0;
+  const int64_t s0 = s00 + z * ns;
+  Sink out = out0;
+  if (out.D) out.D += z * zstride;
   const int t = threadIdx.x;
   const int ty = t >> 4, tx = t & 15;
   const int w = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
@@ -762,6 +771,29 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
   }
 }
 
+// The ordered reduction of split-K partial results P[0..runs) (each M x N):
+// D = ((P0 + P1) + P2) ... in FP32 round-to-nearest-even, one lane per
+// output, and the per-row XOR of the final D.
+__global__ __launch_bounds__(256) void reduce_runs_kernel(const uint32_t* __restrict__ P,
+                                                         int64_t runs, int64_t M, int64_t N,
+                                                         uint32_t* __restrict__ D,
+                                                         uint32_t* __restrict__ xorsum) {
+  const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
+    uint32_t v = 0;
+    if (col < N) {
+      const int64_t idx = row * N + col;
+      v = P[idx];
+      for (int64_t r = 1; r < runs; ++r) v = fp32_add_rne(v, P[r * M * N + idx]);
+      D[idx] = v;
+    }
+    if (xorsum) {
+      const uint32_t w = wave_xor(v);
+      if ((threadIdx.x & 63) == 0 && w) atomicXor(&xorsum[row], w);
+    }
+  }
+}
+
 }  // namespace fastk
 
 // Shapes the tiled kernel takes: the GEMM grid is (N blocks, M blocks) and
@@ -783,9 +815,12 @@ inline int64_t gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 // (gemm_fast_workspace_bytes(M, N, 16 * ws_steps) bytes).
 // splits > 1 (a divisor of K/16): the split-K schedule.  Run r chains steps
 // [r*T/splits, (r+1)*T/splits) of the T = K/16 steps, from C for r = 0 and
-// from +0 otherwise; the runs are launched in order and each later one adds
-// its partial result into D (fp32_add_rne), so that D = ((P0 + P1) + P2)...
-// The xorsum, if any, is taken by the last run, over the final D.
+// from +0 otherwise, giving P_r, and D = ((P0 + P1) + P2) ... in FP32
+// round-to-nearest-even (fp32_add_rne).  With a partials buffer of
+// splits x M x N words and images of all T steps, the runs are computed side
+// by side into it and then added in run order (reduce_runs_kernel, which
+// also takes the xorsum); otherwise the runs are launched in order and each
+// later one adds its partial result into D, the last one taking the xorsum.
 // A workspace too small for all T steps is filled once per run, or, when it
 // cannot hold a whole run, run 0 of an emulating call is cut into chunks of
 // ws_steps steps, each restarting from the D that the previous chunk wrote:
@@ -795,7 +830,7 @@ inline int64_t gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 template <int MODEL, int DT>
 inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, const Sink& out,
                              int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_steps,
-                             hipStream_t s, int64_t splits = 1) {
+                             hipStream_t s, int64_t splits = 1, uint32_t* partials = nullptr) {
   const int64_t mb = (M + fastk::BM - 1) / fastk::BM, nb = (N + fastk::BN - 1) / fastk::BN;
   const int64_t nsteps = K / 16, per = nsteps / splits;
   const dim3 grid((unsigned)nb, (unsigned)mb);
@@ -815,14 +850,29 @@ inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, co
                    int64_t istride) {
     if (istride > 0) {
       fastk::gemm_fast_kernel<MODEL, DT, true><<<grid, dim3(fastk::NT), 0, s>>>(
-          A, B, c, o, M, N, K, t0, n, ws_a, ws_b, i0, istride);
+          A, B, c, o, M, N, K, t0, n, ws_a, ws_b, i0, istride, 0);
     } else {
       fastk::gemm_fast_kernel<MODEL, DT, false><<<grid, dim3(fastk::NT), 0, s>>>(
-          A, B, c, o, M, N, K, t0, n, nullptr, nullptr, 0, 0);
+          A, B, c, o, M, N, K, t0, n, nullptr, nullptr, 0, 0, 0);
     }
   };
   const bool whole = ws_steps >= nsteps;
   if (whole) prepass(0, nsteps);
+  if (whole && partials && splits > 1) {
+    // every run at once, each into its own M x N partial result, then the
+    // ordered reduction (and the xorsum of the final D)
+    Sink o = out;
+    o.D = partials;
+    o.xorsum = nullptr;
+    o.accumulate = 0;
+    fastk::gemm_fast_kernel<MODEL, DT, true>
+        <<<dim3((unsigned)nb, (unsigned)mb, (unsigned)splits), dim3(fastk::NT), 0, s>>>(
+            A, B, C, o, M, N, K, 0, per, ws_a, ws_b, 0, nsteps, M * N);
+    const int64_t rows = M < 32768 ? M : 32768;
+    fastk::reduce_runs_kernel<<<dim3((unsigned)((N + 255) / 256), (unsigned)rows), dim3(256),
+                                0, s>>>(partials, splits, M, N, out.D, out.xorsum);
+    return;
+  }
   for (int64_t r = 0; r < splits; ++r) {
     Sink o = out;
     o.accumulate = r > 0;

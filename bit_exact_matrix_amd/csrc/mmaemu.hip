@@ -221,15 +221,32 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
   if (out.report) init_report_kernel<<<dim3(1), dim3(64), 0, s>>>(out.report);
   if (M == 0 || N == 0) return hipGetLastError();
   if (gemm_fast_supported(M, N, K)) {
-    // as many steps of operand images as the cap allows: all K/16, else one
-    // split-K run's worth, else fewer (chunks)
     const int64_t nsteps = K / 16, per = nsteps / splits;
     const int64_t step_bytes = gemm_fast_workspace_bytes(M, N, 16);
-    int64_t ws_steps = workspace_cap() / step_bytes;
-    if (ws_steps > nsteps) ws_steps = nsteps;
-    if (ws_steps < nsteps && ws_steps > per) ws_steps = per;
-    void* ws = ws_steps > 0 ? workspace_alloc(ws_steps * step_bytes, s) : nullptr;
-    gemm_fast_launch<MODEL, DT>(A, B, C, out, M, N, K, ws, ws_steps, s, splits);
+    const int64_t cap = workspace_cap();
+    void* ws = nullptr;
+    int64_t ws_steps = 0;
+    uint32_t* partials = nullptr;
+    // split-K: the runs side by side when the images of all steps and one
+    // M x N partial result per run fit under the cap
+    const int64_t cd = M * N * 4;  // no overflow: checked with the shape
+    if (splits > 1 && out.D && splits <= 65535 && cd <= cap / splits &&
+        nsteps <= (cap - splits * cd) / step_bytes) {
+      ws = workspace_alloc(nsteps * step_bytes + splits * cd, s);
+      if (ws) {
+        ws_steps = nsteps;
+        partials = (uint32_t*)((char*)ws + nsteps * step_bytes);
+      }
+    }
+    if (!ws) {
+      // as many steps of operand images as the cap allows: all K/16, else
+      // one split-K run's worth, else fewer (chunks)
+      ws_steps = cap / step_bytes;
+      if (ws_steps > nsteps) ws_steps = nsteps;
+      if (ws_steps < nsteps && ws_steps > per) ws_steps = per;
+      ws = ws_steps > 0 ? workspace_alloc(ws_steps * step_bytes, s) : nullptr;
+    }
+    gemm_fast_launch<MODEL, DT>(A, B, C, out, M, N, K, ws, ws_steps, s, splits, partials);
     if (ws) {
       // the free is ordered after the kernels; it is issued whatever the
       // launches returned, so that a failed call does not hold the memory

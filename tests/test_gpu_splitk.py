@@ -64,3 +64,35 @@ def test_splitk_full_size_sampled_rows(torch_dev, orc):
         want, wx = orc.gemm_splitk(model, dt, A[r0:r1], B, C[r0:r1], 4)
         assert_bits_equal(got[r0:r1], want, f"split-K full rows {r0}:{r1}")
         assert_bits_equal(gx[r0:r1], wx, f"split-K full xorsum rows {r0}:{r1}")
+
+
+@pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("hopper", "bf16"),
+                                      ("hopper", "e4m3")])
+def test_many_runs_side_by_side(torch_dev, orc, model, dt):
+    """Small M x N, long K: the runs are computed side by side into partial
+    results and added in run order; up to one K-step per run.  In place too,
+    and again with a workspace cap that forces the runs one after another."""
+    import os
+    torch, dev = torch_dev
+    M, N, K = 70, 90, 1024                 # 64 K-steps
+    A, B, C = _gen("specials", model, dt, M, N, K, 8200)
+    for splits in (2, 16, 64):
+        want, wx = orc.gemm_splitk(model, dt, A, B, C, splits)
+        say("split-K side by side", model, dt, splits)
+        got, gx = run_splitk(torch_dev, model, dt, A, B, C, splits)
+        assert_bits_equal(got, want, f"side by side {model}/{dt} splits={splits}")
+        assert_bits_equal(gx, wx, f"side by side {model}/{dt} splits={splits} xorsum")
+        tC = to_dev(torch_dev, C)
+        D, X = mm.gemm(model, dt, to_dev(torch_dev, A), to_dev(torch_dev, B), tC, D=tC,
+                       xorsum=True, splits=splits)
+        assert_bits_equal(to_host_bits(D), want, f"side by side in place splits={splits}")
+        assert_bits_equal(to_host_bits(X), wx, f"side by side in place splits={splits} xorsum")
+    # images of all 64 steps fit, the 16 partial results do not: runs in order
+    os.environ["MMAEMU_WORKSPACE_MAX_BYTES"] = str(64 * 12 * 1024 * 4 + 4 * M * N * 4)
+    try:
+        want, wx = orc.gemm_splitk(model, dt, A, B, C, 16)
+        got, gx = run_splitk(torch_dev, model, dt, A, B, C, 16)
+    finally:
+        del os.environ["MMAEMU_WORKSPACE_MAX_BYTES"]
+    assert_bits_equal(got, want, f"runs in order {model}/{dt}")
+    assert_bits_equal(gx, wx, f"runs in order {model}/{dt} xorsum")
