@@ -138,8 +138,11 @@ int mma_emulate_gemm_async(int model, int dtype, const void *A, const void *B,
  * The xorsum fingerprint is taken over the final D.  Arguments, layouts,
  * aliasing (D == C allowed), workspace and errors as for
  * mma_emulate_gemm_async; splits < 1 or not dividing K/16 (or splits != 1
- * with K = 0) is MMAEMU_ERR_SHAPE.  Enqueued on hip_stream; returns after
- * enqueue. */
+ * with K = 0) is MMAEMU_ERR_SHAPE.  Workspace: when the operand images of
+ * all K/16 steps and splits x M x N x 4 bytes of partial results fit under
+ * the same cap (and splits <= 65535), the runs are computed side by side
+ * and then added in run order; otherwise they run one after another.  The
+ * results are the same.  Enqueued on hip_stream; returns after enqueue. */
 int mma_emulate_gemm_splitk_async(int model, int dtype, const void *A,
                                   const void *B, const float *C, float *D,
                                   int64_t M, int64_t N, int64_t K, int64_t splits,
