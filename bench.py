@@ -108,10 +108,53 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU work for the oracle sample")
     p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--valu-peak", action="store_true",
+                   help="instead of a workload, measure the issue rate of the hot loop's "
+                        "VALU instructions (libvalurate.so) against the derived peak")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, run a plain 256 MiB device copy twice "
                         "(reference kernel for scaling HBM byte counters)")
     return p.parse_args()
+
+
+def bench_valu_peak(args):
+    """Issue rate of each 32-bit VALU instruction the hot loop is built
+    from (probe/valu_rate.hip: dependency chains of one instruction, many
+    waves per SIMD), in lane operations per second, against the peak derived
+    from the unit counts and the clock."""
+    import ctypes
+
+    path = os.path.join(ROOT, "bit_exact_matrix_amd", "probe", "libvalurate.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first (__graft_entry__.build())")
+    import torch
+    torch.cuda.init()
+    lib = ctypes.CDLL(path)
+    lib.valu_rate_run.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.POINTER(ctypes.c_double)]
+    lib.valu_rate_name.restype = ctypes.c_char_p
+    iters, blocks = 4096, 256 * 16
+    lanes_ops = 32 * iters * blocks * 256
+    rates = {}
+    for op in range(lib.valu_rate_nops()):
+        ms = ctypes.c_double(0.0)
+        rc = lib.valu_rate_run(op, iters, blocks, max(1, args.steps), ctypes.byref(ms))
+        if rc != 0:
+            raise RuntimeError(f"valu_rate_run({op}) returned {rc}")
+        rates[lib.valu_rate_name(op).decode()] = lanes_ops / (ms.value / 1e3)
+    first = "v_add_u32"
+    out = {
+        "metric": "VALU issue rate, lane operations per second, by instruction",
+        "value": round(rates[first], 1), "unit": "lane-op/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": 1, "higher_is_better": True, "vs_baseline": None,
+        "dtype": "int32", "data": "synthetic",
+        "config": {"workload": "valu_issue_rate_probe", "lanes": blocks * 256,
+                   "instructions_per_lane": 32 * iters, "chains_per_lane": 8},
+        "peak_derived": VALU_PEAK_OPS,
+        "rates": {k: round(v, 1) for k, v in rates.items()},
+        "frac_of_derived_peak": {k: round(v / VALU_PEAK_OPS, 4) for k, v in rates.items()},
+    }
+    print(json.dumps(out), flush=True)
 
 
 def profile_record(name, kernel_hash):
@@ -245,6 +288,8 @@ def main():
               "(the GEMM would shard over rows of D, with no exchange between GPUs).",
               file=sys.stderr)
         sys.exit(2)
+    if args.valu_peak:
+        return bench_valu_peak(args)
     if args.workload in TILE_WORKLOADS:
         if args.verify or args.splits != 1:
             print("--verify and --splits apply to the GEMM workloads", file=sys.stderr)

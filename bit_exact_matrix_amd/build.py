@@ -1,4 +1,4 @@
-"""Build libmmaemu.so in-tree with hipcc for gfx950."""
+"""Build libmmaemu.so (and the VALU issue-rate probe) in-tree with hipcc for gfx950."""
 from __future__ import annotations
 
 import os
@@ -27,8 +27,11 @@ def hipcc() -> str:
     return "hipcc"
 
 
-def build(out: str = OUT, verbose: bool = False) -> str:
-    src = os.path.join(CSRC, "mmaemu.hip")
+PROBE_SRC = os.path.join(HERE, "probe", "valu_rate.hip")
+PROBE_OUT = os.path.join(HERE, "probe", "libvalurate.so")
+
+
+def _hipcc(src: str, out: str, verbose: bool) -> str:
     tmp = out + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, src, "-o", tmp]
     if verbose:
@@ -36,9 +39,16 @@ def build(out: str = OUT, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         sys.stderr.write(r.stdout + r.stderr)
-        raise RuntimeError("hipcc failed building libmmaemu.so")
+        raise RuntimeError(f"hipcc failed building {os.path.basename(out)}")
     os.replace(tmp, out)
     return out
+
+
+def build(out: str = OUT, verbose: bool = False) -> str:
+    """libmmaemu.so (the library) and libvalurate.so (the VALU issue-rate
+    probe that bench.py --valu-peak runs)."""
+    _hipcc(PROBE_SRC, PROBE_OUT, verbose)
+    return _hipcc(os.path.join(CSRC, "mmaemu.hip"), out, verbose)
 
 
 if __name__ == "__main__":

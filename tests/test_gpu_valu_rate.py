@@ -1,0 +1,45 @@
+"""The VALU roofline's peak against measurement.  The issue-rate probe
+(bit_exact_matrix_amd/probe/valu_rate.hip) runs dependency chains of one
+instruction at a time.  The instructions that carry the hot loop's per-MAC
+work (exact product, sign-and-accumulate, the packed exponent add and
+maximum, the word-select shift) and its normalisation must issue at the
+peak derived from the unit counts and the clock (one wave64 instruction per
+SIMD every 4 cycles), within a few per cent, and never above it.  A few
+simple 32-bit operations issue faster on gfx950; for them only the lower
+bound is checked."""
+import ctypes
+import os
+
+import pytest
+
+from test_gpu_parity import say, torch_dev  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PEAK = 256 * 4 * 16 * 2.4e9   # CUs x SIMDs x lanes x clock: 32-bit lane operations per second
+AT_PEAK = {"v_mad_i32_i24", "v_xad_u32", "v_pk_add_u16", "v_pk_minimum3_f16",
+           "v_ashrrev_i32_sdwa", "v_bcnt_u32_b32", "v_ffbh_u32", "v_and_or_b32",
+           "v_perm_b32", "v_lshlrev_b32", "v_max_i32"}
+
+
+def test_issue_rates_against_the_derived_peak(torch_dev):
+    path = os.path.join(ROOT, "bit_exact_matrix_amd", "probe", "libvalurate.so")
+    assert os.path.exists(path), "libvalurate.so is not built"
+    lib = ctypes.CDLL(path)
+    lib.valu_rate_run.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int64, ctypes.c_int,
+                                  ctypes.POINTER(ctypes.c_double)]
+    lib.valu_rate_name.restype = ctypes.c_char_p
+    iters, blocks = 2048, 4096
+    seen = set()
+    for op in range(lib.valu_rate_nops()):
+        ms = ctypes.c_double(0.0)
+        assert lib.valu_rate_run(op, iters, blocks, 5, ctypes.byref(ms)) == 0
+        rate = 32 * iters * blocks * 256 / (ms.value / 1e3)
+        name = lib.valu_rate_name(op).decode()
+        seen.add(name)
+        say("VALU issue rate", name, f"{rate / 1e12:.2f}e12 lane-op/s", f"{rate / PEAK:.3f} of peak")
+        assert rate >= 0.9 * PEAK, f"{name} reaches only {rate / PEAK:.2f} of the peak"
+        if name in AT_PEAK:
+            assert rate <= 1.02 * PEAK, f"{name} runs above the derived peak: {rate:.3e}"
+    assert AT_PEAK <= seen
