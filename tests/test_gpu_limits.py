@@ -73,3 +73,19 @@ def test_long_chain(torch_dev, orc, model, dt):
                    to_dev(torch_dev, C), xorsum=True)
     assert_bits_equal(to_host_bits(D), want, f"long chain {model}/{dt}")
     assert_bits_equal(to_host_bits(X), wx, f"long chain {model}/{dt} xorsum")
+
+
+def test_split_k_past_the_grid_limit(torch_dev, orc):
+    """Split-K on a shape the tiled kernel does not take: the one-lane-per-
+    output kernel runs the two runs in order and adds the second into D."""
+    rows, N, K = LIMIT + 64, 16, 32
+    A0, B, C0 = I.gemm_normal(9450, PERIOD, N, K, I.FP16, c_zero=False)
+    reps = -(-rows // PERIOD)
+    A = _periodic(A0, reps, 0)[:rows]
+    C = _periodic(C0, reps, 0)[:rows]
+    D0, x0 = orc.gemm_splitk("hopper", "fp16", A0, B, C0, 2)
+    say("split-K past the grid limit", rows, N, K)
+    D, X = mm.gemm("hopper", "fp16", to_dev(torch_dev, A), to_dev(torch_dev, B),
+                   to_dev(torch_dev, C), xorsum=True, splits=2)
+    assert_bits_equal(to_host_bits(D), _periodic(D0, reps, 0)[:rows], "split-K tall")
+    assert_bits_equal(to_host_bits(X), np.tile(x0, reps)[:rows], "split-K tall xorsum")
