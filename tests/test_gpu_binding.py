@@ -45,3 +45,51 @@ def test_operand_checks(torch_dev):
         mm.gemm("ampere", "fp16", a, a, C=torch.zeros((32, 32)))
     with pytest.raises(ValueError, match="shape"):
         mm.gemm("ampere", "fp16", a, a, C=torch.zeros((32, 31), device=dev))
+
+
+def test_concurrent_calls_from_host_threads(torch_dev, orc):
+    """Four host threads, each on its own stream, emulate different GEMMs
+    (with the workspace, split-K runs side by side, and tiles) at the same
+    time; every result must be the oracle's."""
+    import threading
+    torch, dev = torch_dev
+    cases = []
+    for i in range(4):
+        A, B, C = I.gemm_normal(9650 + i, 130 + 17 * i, 150, 256, I.FP16, c_zero=False)
+        want, wx = (orc.gemm("hopper", "fp16", A, B, C) if i % 2 == 0
+                    else orc.gemm_splitk("hopper", "fp16", A, B, C, 4))
+        cases.append((A, B, C, want, wx, 1 if i % 2 == 0 else 4))
+    At, Bt, Ct = I.tiles_normal(9660, 333)
+    wt, wtx = orc.tiles("ampere", "fp16", At, Bt, Ct)
+    results, errors = {}, []
+
+    def work(i):
+        try:
+            s = torch.cuda.Stream(device=dev)
+            with torch.cuda.stream(s):
+                A, B, C, _, _, splits = cases[i]
+                tA, tB, tC = to_dev(torch_dev, A), to_dev(torch_dev, B), to_dev(torch_dev, C)
+                for _ in range(5):
+                    D, X = mm.gemm("hopper", "fp16", tA, tB, tC, xorsum=True, splits=splits,
+                                   stream=s)
+                    Dt, Xt = mm.tiles("ampere", "fp16", to_dev(torch_dev, At),
+                                      to_dev(torch_dev, Bt), to_dev(torch_dev, Ct),
+                                      xorsum=True, stream=s)
+            s.synchronize()
+            results[i] = (D, X, Dt, Xt)
+        except Exception as e:     # reported in the main thread
+            errors.append((i, repr(e)))
+
+    say("concurrent host threads")
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i, (_, _, _, want, wx, _) in enumerate(cases):
+        D, X, Dt, Xt = results[i]
+        assert_bits_equal(to_host_bits(D), want, f"thread {i} gemm")
+        assert_bits_equal(to_host_bits(X), wx, f"thread {i} gemm xorsum")
+        assert_bits_equal(to_host_bits(Dt), wt, f"thread {i} tiles")
+        assert_bits_equal(to_host_bits(Xt), wtx, f"thread {i} tiles xorsum")
