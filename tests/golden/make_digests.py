@@ -2,6 +2,12 @@
 the seeded workloads, so GPU tests can check full-size results bit for bit
 without re-running the oracle for minutes.  Calls only oracle/ and the seeded
 input generators.  Run:  python tests/golden/make_digests.py [names...]
+
+Each entry is keyed by what determines it: the digest of its input bits
+(A, B, C from the seeded generator) and the digest of the oracle's sources.
+tests/test_oracle_digests.py checks both against the current tree, so that
+a cache made by another oracle or from other inputs cannot pass for this
+one's.
 """
 import hashlib
 import json
@@ -22,6 +28,23 @@ OUT = os.path.join(os.path.dirname(os.path.abspath(__file__)), "oracle_digests.j
 
 def sha(a):
     return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+ORACLE_SOURCES = ("oracle/mma_oracle.c", "oracle/mma_oracle.h", "oracle/__init__.py")
+
+
+def oracle_source_sha256():
+    h = hashlib.sha256()
+    for rel in ORACLE_SOURCES:
+        h.update(rel.encode() + b"\0" + open(os.path.join(ROOT, rel), "rb").read() + b"\0")
+    return h.hexdigest()
+
+
+def inputs_sha256(A, B, C):
+    h = hashlib.sha256()
+    for a in (A, B, C):
+        h.update(np.ascontiguousarray(a).tobytes())
+    return h.hexdigest()
 
 
 def workloads():
@@ -69,7 +92,9 @@ def main(names):
                       "D_head": [f"{int(v):#010x}" for v in D.reshape(-1)[:4]],
                       "n_inf": int(((D & 0x7FFFFFFF) == 0x7F800000).sum()),
                       "n_nan": int(((D & 0x7FFFFFFF) > 0x7F800000).sum()),
-                      "oracle_seconds": round(dt_s, 1), "oracle_threads": oracle.num_cpus()}
+                      "oracle_seconds": round(dt_s, 1), "oracle_threads": oracle.num_cpus(),
+                      "inputs_sha256": inputs_sha256(A, B, C),
+                      "oracle_source_sha256": oracle_source_sha256()}
         print(name, data[name], flush=True)
         json.dump(data, open(OUT, "w"), indent=1, sort_keys=True)
 
