@@ -10,7 +10,7 @@ import pytest
 
 import bit_exact_matrix_amd as mm  # noqa: F401
 from bit_exact_matrix_amd import inputs as I
-from test_gpu_parity import (COMBOS, DT, assert_bits_equal, no_workspace,  # noqa: F401
+from test_gpu_parity import (COMBOS, DT, assert_bits_equal, gemm_kernel, no_workspace,  # noqa: F401
                              run_gemm, say, torch_dev)
 
 pytestmark = pytest.mark.gpu
@@ -26,7 +26,7 @@ def _shapes(seed, n):
 
 @pytest.mark.parametrize("model,dt", COMBOS + [("lovelace", "bf16")])
 @pytest.mark.parametrize("mode", MODES)
-def test_adversarial_random_shapes(torch_dev, orc, model, dt, mode):
+def test_adversarial_random_shapes(torch_dev, orc, gemm_kernel, model, dt, mode):
     for i, (M, N, K) in enumerate(_shapes(zlib.crc32(f"{model}/{dt}/{mode}".encode()), 6)):
         seed = 9000 + 100 * MODES.index(mode) + i
         A, B, C = I.gemm_adversarial(seed, M, N, K, DT[dt], mode)

@@ -14,8 +14,8 @@ import pytest
 
 import bit_exact_matrix_amd as mm
 from bit_exact_matrix_amd import inputs as I
-from test_gpu_parity import (assert_bits_equal, say, to_dev, to_host_bits,  # noqa: F401
-                             torch_dev)
+from test_gpu_parity import (assert_bits_equal, gemm_kernel, say, to_dev,  # noqa: F401
+                             to_host_bits, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,7 @@ def test_wide_gemm_at_the_grid_limit(torch_dev, orc, cols):
 
 
 @pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("hopper", "e4m3")])
-def test_long_chain(torch_dev, orc, model, dt):
+def test_long_chain(torch_dev, orc, gemm_kernel, model, dt):
     M, N, K = 64, 64, 65536
     A, B, C = (I.gemm_e4m3(9500, M, N, K) if dt == "e4m3"
                else I.gemm_normal(9500, M, N, K, I.FP16, c_zero=False))

@@ -138,7 +138,7 @@ def _gen(kind, model, dt, M, N, K, seed):
 
 
 @pytest.mark.parametrize("dt", ["fp16", "bf16"])
-def test_lovelace_gemm_and_tiles(torch_dev, orc, dt):
+def test_lovelace_gemm_and_tiles(torch_dev, orc, gemm_kernel, dt):
     """Lovelace runs the Ampere arithmetic: GEMMs and tiles against the
     oracle's Lovelace model."""
     for si, (M, N, K) in enumerate([(17, 33, 48), (130, 100, 160)]):
@@ -159,7 +159,7 @@ def test_lovelace_gemm_and_tiles(torch_dev, orc, dt):
 
 @pytest.mark.parametrize("model,dt", COMBOS)
 @pytest.mark.parametrize("kind", ["normal", "wide", "specials"])
-def test_gemm_small_full_compare(torch_dev, orc, model, dt, kind):
+def test_gemm_small_full_compare(torch_dev, orc, gemm_kernel, model, dt, kind):
     for si, (M, N, K) in enumerate(SHAPES):
         A, B, C = _gen(kind, model, dt, M, N, K, 1000 + si)
         say("gemm", model, dt, kind, (M, N, K))
@@ -170,7 +170,7 @@ def test_gemm_small_full_compare(torch_dev, orc, model, dt, kind):
 
 
 @pytest.mark.parametrize("model,dt", COMBOS)
-def test_gemm_edge_cases(torch_dev, orc, model, dt):
+def test_gemm_edge_cases(torch_dev, orc, gemm_kernel, model, dt):
     torch, dev = torch_dev
     M, N, K = 33, 47, 64
     A, B, C = _gen("normal", model, dt, M, N, K, 77)
@@ -238,11 +238,26 @@ def test_gemm_full_size(torch_dev, orc, name):
 # --------------------------------------- the kernel that unpacks in place
 @pytest.fixture
 def no_workspace():
-    """Force the GEMM path that needs no pre-pass workspace (the library
-    reads MMAEMU_NO_WORKSPACE on every call)."""
+    """Force the tiled kernel's variant that needs no pre-pass workspace (the
+    library reads MMAEMU_NO_WORKSPACE and MMAEMU_NARROW_BLOCKS on every call;
+    0 keeps small shapes off the narrow kernel)."""
     os.environ["MMAEMU_NO_WORKSPACE"] = "1"
+    os.environ["MMAEMU_NARROW_BLOCKS"] = "0"
     yield
     del os.environ["MMAEMU_NO_WORKSPACE"]
+    del os.environ["MMAEMU_NARROW_BLOCKS"]
+
+
+@pytest.fixture(params=["tiled", "narrow"])
+def gemm_kernel(request):
+    """Run a test once on each GEMM kernel: the tiled one (4x4 outputs per
+    lane) and the narrow one (one output per lane), which the library takes
+    for plain chains with few 64x64 blocks.  MMAEMU_NARROW_BLOCKS is the
+    block-count threshold: 0 never takes the narrow kernel, a huge value
+    always (where it applies)."""
+    os.environ["MMAEMU_NARROW_BLOCKS"] = "0" if request.param == "tiled" else str(1 << 40)
+    yield request.param
+    del os.environ["MMAEMU_NARROW_BLOCKS"]
 
 
 @pytest.mark.parametrize("model,dt", COMBOS)

@@ -109,3 +109,52 @@ def test_largest_group_sums(torch_dev, orc, model, dt):
                    to_dev(torch_dev, Cg), xorsum=True)
     assert_bits_equal(to_host_bits(D), want, f"largest sums gemm {model}/{dt}")
     assert_bits_equal(to_host_bits(X), wx, f"largest sums gemm xorsum {model}/{dt}")
+
+
+def _cancelling_specials(model, dt, n_rows, seed):
+    """A, B, C of shape n_rows x 64 x 32 (or tiles) in which every output of
+    rows 0..3 has, in the first K-step, (-inf)*(-0) at k = 1 and (-0)*NaN at
+    k = 2: two inf/NaN products with equal exponent codes and opposite
+    signs, which cancel exactly in a fixed-width sum.  IEEE and the oracle
+    make every such output NaN."""
+    from test_gpu_parity import _gen
+    A, B, C = _gen("normal", model, dt, n_rows, 64, 32, seed)
+    if dt == "fp16":
+        ninf, nzero, nan = 0xFC00, 0x8000, 0x7C01
+    else:
+        ninf, nzero, nan = 0xFF80, 0x8000, 0x7FC1
+    A[0:4, 1], A[0:4, 2] = ninf, nzero
+    B[1, :], B[2, :] = nzero, nan
+    return A, B, C
+
+
+@pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("ampere", "bf16"),
+                                      ("hopper", "fp16")])
+@pytest.mark.parametrize("variant", ["tiled", "tiled-no-workspace", "narrow"])
+def test_cancelling_inf_nan_products(torch_dev, orc, model, dt, variant):
+    import os
+    A, B, C = _cancelling_specials(model, dt, 64, 9950)
+    want, wx = orc.gemm(model, dt, A, B, C)
+    assert np.all(want == 0x7FC00000), "the construction must give NaN everywhere"
+    os.environ["MMAEMU_NARROW_BLOCKS"] = str(1 << 40) if variant == "narrow" else "0"
+    if variant == "tiled-no-workspace":
+        os.environ["MMAEMU_NO_WORKSPACE"] = "1"
+    try:
+        say("cancelling inf/NaN products", model, dt, variant)
+        D, X = mm.gemm(model, dt, to_dev(torch_dev, A), to_dev(torch_dev, B),
+                       to_dev(torch_dev, C), xorsum=True)
+        got, gx = to_host_bits(D), to_host_bits(X)
+    finally:
+        del os.environ["MMAEMU_NARROW_BLOCKS"]
+        os.environ.pop("MMAEMU_NO_WORKSPACE", None)
+    assert_bits_equal(got, want, f"cancelling specials {model}/{dt}/{variant}")
+    assert_bits_equal(gx, wx, f"cancelling specials {model}/{dt}/{variant} xorsum")
+    # the same first K-step as independent tiles
+    At = np.ascontiguousarray(A[:64, :16].reshape(4, 16, 16))
+    Bt = np.ascontiguousarray(np.broadcast_to(B[:16, :16], (4, 16, 16)))
+    Ct = np.ascontiguousarray(C[:64, :16].reshape(4, 16, 16))
+    wt, wtx = orc.tiles(model, dt, At, Bt, Ct)
+    Dt, Xt = mm.tiles(model, dt, to_dev(torch_dev, At), to_dev(torch_dev, Bt),
+                      to_dev(torch_dev, Ct), xorsum=True)
+    assert_bits_equal(to_host_bits(Dt), wt, f"cancelling specials tiles {model}/{dt}")
+    assert_bits_equal(to_host_bits(Xt), wtx, f"cancelling specials tiles {model}/{dt} xorsum")

@@ -10,7 +10,7 @@ import pytest
 
 import bit_exact_matrix_amd as mm
 from test_gpu_parity import (COMBOS, DIGESTS, FULL, _gen, say, sha, to_dev,  # noqa: F401
-                             to_host_bits, torch_dev, no_workspace)
+                             to_host_bits, torch_dev, no_workspace, gemm_kernel)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +39,7 @@ def check(torch_dev, orc, model, dt, A, B, C, D_oracle, claimed, what):
 
 @pytest.mark.parametrize("model,dt", COMBOS)
 @pytest.mark.parametrize("kind", ["normal", "specials"])
-def test_verify_matches_oracle(torch_dev, orc, model, dt, kind):
+def test_verify_matches_oracle(torch_dev, orc, gemm_kernel, model, dt, kind):
     rng = np.random.default_rng(4242)
     for si, (M, N, K) in enumerate([(17, 33, 48), (130, 100, 160), (129, 257, 96)]):
         A, B, C = _gen(kind, model, dt, M, N, K, 6000 + si)
@@ -62,7 +62,7 @@ def test_verify_in_place_unpack_path(torch_dev, orc, no_workspace, model, dt):
               f"verify/no-ws {model}/{dt} plants={n}")
 
 
-def test_verify_k0_is_c_and_inputs_may_overlap(torch_dev, orc):
+def test_verify_k0_is_c_and_inputs_may_overlap(torch_dev, orc, gemm_kernel):
     """K = 0: the emulated D is C.  The claimed D may be the very buffer C."""
     torch, dev = torch_dev
     rng = np.random.default_rng(5)
@@ -118,7 +118,7 @@ def test_verify_full_size(torch_dev, orc, name):
         assert np.array_equal(to_host_bits(X), want[2])
 
 
-def test_verify_xor_blind_spot(torch_dev, orc):
+def test_verify_xor_blind_spot(torch_dev, orc, gemm_kernel):
     """The same flip in two elements of one row: the row word cancels to 0,
     the count and first index still report both."""
     M, N, K = 20, 40, 32

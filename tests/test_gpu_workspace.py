@@ -25,10 +25,14 @@ def step_bytes(M, N):
 
 @pytest.fixture
 def cap():
+    """Sets the cap; small shapes stay on the tiled kernel (the narrow one
+    takes no workspace)."""
     def set_cap(nbytes):
         os.environ["MMAEMU_WORKSPACE_MAX_BYTES"] = str(nbytes)
+    os.environ["MMAEMU_NARROW_BLOCKS"] = "0"
     yield set_cap
     os.environ.pop("MMAEMU_WORKSPACE_MAX_BYTES", None)
+    del os.environ["MMAEMU_NARROW_BLOCKS"]
 
 
 def run(torch_dev, model, dt, A, B, C, splits=1, in_place=False):
