@@ -5,7 +5,8 @@ Each mutant is a textual edit of oracle/mma_oracle.c compiled into a
 temporary library; the original is never touched.  The battery run against
 each mutant uses only the page-derived and mathematical pins of
 test_oracle_pins.py (hand-derived values, neutral subgroups, library casts,
-the exact-integer closed form, invariants) -- not the rational model.
+the exact-integer closed form, IEEE special values, invariants) -- not the
+rational model.
 """
 import os
 import shutil
@@ -61,6 +62,11 @@ MUTANTS = {
                             "  if (0) {")],
     "cancellation_gives_minus_zero": [("  g.zero_sign = 0; /* exact cancellation gives +0 */",
                                        "  g.zero_sign = 1;")],
+    "inf_times_zero_is_zero": [("(a.kind == K_ZERO && b.kind == K_INF)) {\n    p.kind = K_NAN;",
+                                "(a.kind == K_ZERO && b.kind == K_INF)) {\n    p.kind = K_ZERO;")],
+    "opposite_infs_give_inf": [("if (any_nan || (pos_inf && neg_inf)) return CANONICAL_NAN;",
+                                "if (any_nan) return CANONICAL_NAN;")],
+    "nan_C_ignored": [("  if (C.kind == K_NAN) any_nan = 1;\n", "")],
 }
 
 
@@ -92,6 +98,9 @@ def _battery(orc):
         checks.append((f"permutation:{model}:{dt}",
                        lambda m=model, d=dt: P.test_permutation_within_groups(orc, m, d)))
     checks.append(("zero_sign", lambda: _zero_sign(orc)))
+    for case in P.SPECIAL_CASES:
+        checks.append(("special:" + case[0],
+                       lambda c=case: P.test_special_values_follow_ieee(orc, c)))
     for name, fn in checks:
         try:
             fn()
