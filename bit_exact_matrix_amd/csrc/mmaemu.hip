@@ -239,7 +239,10 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
   }
   if (out.report) init_report_kernel<<<dim3(1), dim3(64), 0, s>>>(out.report);
   if (M == 0 || N == 0) return hipGetLastError();
-  if (gemm_fast_supported(M, N, K) && splits == 1 && M * N / 4096 < narrow_blocks()) {
+  // (the narrow grid's y dimension, 16 rows a block, stays within 65,535
+  // blocks, as the tiled grid's does; a taller shape runs tiled)
+  if (gemm_fast_supported(M, N, K) && splits == 1 && (M + 15) / 16 <= 65535 &&
+      M * N / 4096 < narrow_blocks()) {
     narrowk::gemm_narrow_kernel<MODEL, DT>
         <<<dim3((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), dim3(256), 0, s>>>(
             A, B, C, out, M, N, K, 0, K / 16);

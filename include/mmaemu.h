@@ -55,8 +55,9 @@
  *   calls.  GEMMs with fewer than 192 x 4096 outputs (M * N) run on a
  *   kernel with one lane per output, which needs no workspace; the
  *   environment variable MMAEMU_NARROW_BLOCKS sets that threshold in units
- *   of 4096 outputs (0: never), read on every call.  Either way the
- *   results are the same.
+ *   of 4096 outputs (0: never), read on every call; shapes over 1,048,560
+ *   rows always run on the other kernels.  Either way the results are the
+ *   same.
  *   A  M x K row-major raw codes: uint16 (FP16, BF16) or uint8 (E4M3)
  *   B  K x N row-major raw codes, same type
  *   C  M x N row-major FP32 (read as bit patterns); NULL means all +0.0
