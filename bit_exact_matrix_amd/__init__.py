@@ -117,8 +117,12 @@ def mma_emulate_spec_version() -> int:
 
 
 # ------------------------------------------------------------ torch layer
-def _enum(v, table):
-    return table[v.lower()] if isinstance(v, str) else int(v)
+def _enum(v, table, what):
+    if isinstance(v, str):
+        if v.lower() not in table:
+            raise ValueError(f"unknown {what} {v!r}: one of {', '.join(sorted(table))}")
+        return table[v.lower()]
+    return int(v)
 
 
 def _dev_ptr(t, what, nbytes_elem=None, device=None):
@@ -157,6 +161,9 @@ def _launch(A, stream):
 
 
 def _matrix_shapes(A, B):
+    import torch
+    if not isinstance(B, torch.Tensor):
+        raise TypeError("B must be a device tensor")
     if A.dim() != 2 or B.dim() != 2:
         raise ValueError("A and B must be matrices")
     M, K = A.shape
@@ -176,7 +183,7 @@ def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None, splits=1
     patterns of the per-row XOR) or None.
     """
     import torch
-    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    m, d = _enum(model, MODELS, "model"), _enum(dtype, DTYPES, "dtype")
     esz = 1 if d == FP8_E4M3 else 2
     dev, s = _launch(A, stream)
     M, N, K = _matrix_shapes(A, B)
@@ -206,7 +213,7 @@ def verify(model, dtype, A, B, C, D_claimed, row_diff=False, stream=None):
     None.  ``mismatches(report)`` turns the report into Python ints.
     """
     import torch
-    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    m, d = _enum(model, MODELS, "model"), _enum(dtype, DTYPES, "dtype")
     esz = 1 if d == FP8_E4M3 else 2
     dev, s = _launch(A, stream)
     M, N, K = _matrix_shapes(A, B)
@@ -234,9 +241,11 @@ def mismatches(report):
 def tiles(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None):
     """ntiles independent 16x16x16 MMAs: A, B [n,16,16] codes, C [n,16,16] f32."""
     import torch
-    m, d = _enum(model, MODELS), _enum(dtype, DTYPES)
+    m, d = _enum(model, MODELS, "model"), _enum(dtype, DTYPES, "dtype")
     esz = 1 if d == FP8_E4M3 else 2
     dev, s = _launch(A, stream)
+    if not isinstance(B, torch.Tensor):
+        raise TypeError("B must be a device tensor")
     n = A.shape[0] if A.dim() == 3 else -1
     if tuple(A.shape) != (n, 16, 16) or tuple(B.shape) != (n, 16, 16):
         raise ValueError("A and B must be [ntiles, 16, 16]")

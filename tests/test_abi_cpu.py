@@ -122,3 +122,16 @@ def test_torch_wrappers_reject_host_tensors_before_any_launch():
         mm._matrix_shapes(a.reshape(1, 16, 16), a)
     with pytest.raises(ValueError, match="inner dimensions"):
         mm._matrix_shapes(torch.zeros((16, 32)), torch.zeros((16, 16)))
+    with pytest.raises(TypeError, match="B must be"):
+        mm._matrix_shapes(a, a.numpy())
+
+
+def test_torch_wrappers_reject_unknown_model_and_dtype_names():
+    import torch
+    a = torch.zeros((16, 16), dtype=torch.int16)
+    with pytest.raises(ValueError, match="unknown model 'volta'"):
+        mm.gemm("volta", "fp16", a, a)
+    with pytest.raises(ValueError, match="unknown dtype 'fp32'"):
+        mm.tiles("hopper", "fp32", a.reshape(1, 16, 16), a.reshape(1, 16, 16))
+    with pytest.raises(ValueError, match="unknown model"):
+        mm.verify("", "bf16", a, a, None, torch.zeros((16, 16)))
