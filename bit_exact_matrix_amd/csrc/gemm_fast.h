@@ -184,9 +184,10 @@ __device__ __forceinline__ uint32_t state_to_bits(int X, uint32_t ne) {
 
 // Recompute one output's step from the raw codes in global memory (rare
 // path): output (r, c) of the calling lane's 4x4 tile in the workgroup's
-// 64x64 block.  Rows and columns outside the matrix read as +0 codes.  The
-// row and column are derived here rather than passed, so that the caller
-// keeps no per-lane 64-bit indices live across its loop.
+// 64x64 block.  Rows and columns outside the matrix read the code of 1.0
+// (PAD_CODE), as in the image builders.  The row and column are derived
+// here rather than passed, so that the caller keeps no per-lane 64-bit
+// indices live across its loop.
 template <int MODEL, int DT>
 __device__ __noinline__ uint2 slow_step(const void* A, const void* B, int64_t M, int64_t N,
                                         int64_t K, int64_t s, int tr, int tc, int Xold,
@@ -286,7 +287,7 @@ __device__ __forceinline__ void produce(ST* st, const uint32_t (&ca)[4],
   }
 }
 
-// Global loads of step s for lane t (zero codes outside the matrix).
+// Global loads of step s for lane t (the code of 1.0 outside the matrix).
 template <int DT>
 __device__ __forceinline__ void fetch(const void* A, const void* B, int64_t M, int64_t N,
                                       int64_t K, int64_t bm, int64_t bn, int64_t s, int t,

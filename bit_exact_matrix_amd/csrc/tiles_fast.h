@@ -30,8 +30,11 @@ using namespace fastk;
 constexpr int TPW = 4;  // tiles per wave
 
 // A GEMM stage without the padding of the 12 KiB images (those exist only
-// for whole-image copies): 22,848 bytes, seven waves per CU.
-struct TileImage {
+// for whole-image copies): 22,848 bytes, seven waves per CU.  Declared
+// 16-byte aligned so that the image builder's 16-byte stores stay single
+// b128 writes (at 4-byte alignment each became two two-word writes, whose
+// lanes at k and k + 8 collide on the same LDS banks).
+struct alignas(16) TileImage {
   uint32_t val[16][PAD];
   int32_t sgn[16][PAD];
   uint32_t ne[8][PAD];
