@@ -120,8 +120,9 @@ def parse():
 def bench_valu_peak(args):
     """Issue rate of each 32-bit VALU instruction the hot loop is built
     from (probe/valu_rate.hip: dependency chains of one instruction, many
-    waves per SIMD), in lane operations per second, against the peak derived
-    from the unit counts and the clock."""
+    waves per SIMD), and of the hot loop's pass-2 instruction mix, in lane
+    operations per second, against the peak derived from the unit counts
+    and the clock."""
     import ctypes
 
     path = os.path.join(ROOT, "bit_exact_matrix_amd", "probe", "libvalurate.so")
@@ -134,13 +135,14 @@ def bench_valu_peak(args):
                                   ctypes.POINTER(ctypes.c_double)]
     lib.valu_rate_name.restype = ctypes.c_char_p
     iters, blocks = 4096, 256 * 16
-    lanes_ops = 32 * iters * blocks * 256
+    steps = 32 * iters * blocks * 256      # chain steps per launch, over all lanes
     rates = {}
     for op in range(lib.valu_rate_nops()):
         ms = ctypes.c_double(0.0)
         rc = lib.valu_rate_run(op, iters, blocks, max(1, args.steps), ctypes.byref(ms))
         if rc != 0:
             raise RuntimeError(f"valu_rate_run({op}) returned {rc}")
+        lanes_ops = steps * lib.valu_rate_insts(op)
         rates[lib.valu_rate_name(op).decode()] = lanes_ops / (ms.value / 1e3)
     first = "v_add_u32"
     out = {
@@ -149,7 +151,7 @@ def bench_valu_peak(args):
         "steps": args.steps, "warmup": 1, "higher_is_better": True, "vs_baseline": None,
         "dtype": "int32", "data": "synthetic",
         "config": {"workload": "valu_issue_rate_probe", "lanes": blocks * 256,
-                   "instructions_per_lane": 32 * iters, "chains_per_lane": 8},
+                   "chain_steps_per_lane": 32 * iters, "chains_per_lane": 8},
         "peak_derived": VALU_PEAK_OPS,
         "rates": {k: round(v, 1) for k, v in rates.items()},
         "frac_of_derived_peak": {k: round(v / VALU_PEAK_OPS, 4) for k, v in rates.items()},

@@ -7,6 +7,11 @@
 // Each lane runs eight independent dependency chains of one instruction,
 // 32 instructions per loop iteration; a grid of many waves per SIMD hides
 // the chains' latency, so the loop runs at the instruction's issue rate.
+// One more probe runs the hot loop's own pass-2 mix instead (per two
+// products: two exact products, two alignment shifts, one of them reading
+// its distance from a high word, two sign-and-accumulates and the
+// saturating packed add of both distances): 7 instructions per chain step,
+// 224 per loop iteration.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdio.h>
@@ -30,13 +35,17 @@ enum {
   OP_MAX,        // v_max_i32
   OP_AND_OR,     // v_and_or_b32
   OP_PERM,       // v_perm_b32
+  OP_PASS2_MIX,  // the hot loop's pass-2 sequence (7 instructions)
   NOPS
 };
 const char* const kNames[NOPS] = {
     "v_add_u32",      "v_mad_i32_i24",      "v_xad_u32",       "v_ashrrev_i32",
     "v_pk_add_u16",   "v_pk_minimum3_f16",  "v_bcnt_u32_b32",  "v_ffbh_u32",
     "v_add_u32_e64",  "v_ashrrev_i32_sdwa", "v_xor_b32",       "v_mul_i32_i24",
-    "v_lshlrev_b32",  "v_max_i32",          "v_and_or_b32",    "v_perm_b32"};
+    "v_lshlrev_b32",  "v_max_i32",          "v_and_or_b32",    "v_perm_b32",
+    "pass2_mix"};
+// instructions per chain step
+constexpr int kInsts[NOPS] = {1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 1, 7};
 
 template <int OP>
 __device__ __forceinline__ void step(uint32_t& a, uint32_t b, uint32_t c) {
@@ -74,6 +83,18 @@ __device__ __forceinline__ void step(uint32_t& a, uint32_t b, uint32_t c) {
     asm volatile("v_max_i32 %0, %0, %1" : "+v"(a) : "v"(b));
   } else if constexpr (OP == OP_AND_OR) {
     asm volatile("v_and_or_b32 %0, %0, %1, %2" : "+v"(a) : "v"(b), "v"(c));
+  } else if constexpr (OP == OP_PASS2_MIX) {
+    asm volatile(
+        "v_mad_i32_i24 %0, %0, %1, %2\n"
+        "v_ashrrev_i32 %0, %1, %0\n"
+        "v_xad_u32 %0, %0, %1, %2\n"
+        "v_mad_i32_i24 %0, %0, %1, %2\n"
+        "v_ashrrev_i32_sdwa %0, %1, %0 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:WORD_1 "
+        "src1_sel:DWORD\n"
+        "v_xad_u32 %0, %0, %1, %2\n"
+        "v_pk_add_u16 %0, %0, %1 clamp"
+        : "+v"(a)
+        : "v"(b), "v"(c));
   } else {
     asm volatile("v_perm_b32 %0, %0, %1, %2" : "+v"(a) : "v"(b), "v"(c));
   }
@@ -121,6 +142,7 @@ hipError_t launch_op(int op, uint32_t* out, int64_t iters, int64_t blocks, hipSt
     case OP_LSHL: return launch<OP_LSHL>(out, iters, blocks, s);
     case OP_MAX: return launch<OP_MAX>(out, iters, blocks, s);
     case OP_AND_OR: return launch<OP_AND_OR>(out, iters, blocks, s);
+    case OP_PASS2_MIX: return launch<OP_PASS2_MIX>(out, iters, blocks, s);
     default: return launch<OP_PERM>(out, iters, blocks, s);
   }
 }
@@ -133,8 +155,12 @@ int valu_rate_nops(void) { return NOPS; }
 
 const char* valu_rate_name(int op) { return op >= 0 && op < NOPS ? kNames[op] : "?"; }
 
+// Instructions per chain step of probe `op` (each lane runs 32 * iters
+// steps): 1 for a single instruction, 7 for the pass-2 mix, 0 if unknown.
+int valu_rate_insts(int op) { return op >= 0 && op < NOPS ? kInsts[op] : 0; }
+
 // Times `reps` launches of the probe for instruction `op` (blocks x 256
-// lanes, each lane 32 * iters instructions) after one warm-up launch, on
+// lanes, each lane 32 * iters chain steps) after one warm-up launch, on
 // the current device's null stream.  *best_ms receives the fastest launch.
 // Returns 0, -1 for bad arguments, -2 for a HIP error.
 int valu_rate_run(int op, int64_t iters, int64_t blocks, int reps, double* best_ms) {
