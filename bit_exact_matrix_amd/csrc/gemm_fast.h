@@ -107,6 +107,15 @@ __device__ __forceinline__ uint32_t ffbh(uint32_t x) {
   asm("v_ffbh_u32 %0, %1" : "=v"(r) : "v"(x));
   return r;
 }
+// The leading zeros of x (0xFFFF for x = 0) into the high word of packed,
+// whose low word is kept: an SDWA v_ffbh_u32, so that a pair of counts
+// needs no separate packing instruction.
+__device__ __forceinline__ uint32_t ffbh_into_hi(uint32_t packed, uint32_t x) {
+  asm("v_ffbh_u32_sdwa %0, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+      : "+v"(packed)
+      : "v"(x));
+  return packed;
+}
 // Minimum of three pairs of 16-bit exponent codes.  Every code that reaches
 // it is a positive normal binary16 bit pattern (0x0800 .. 0x6000), and for
 // those the binary16 order is the integer order, so the packed binary16
@@ -562,10 +571,11 @@ __device__ __forceinline__ void normalise2(int S0, int S1, uint32_t mn, int& X0,
                                            uint32_t& NE) {
   const int s0 = S0 >> 31, s1 = S1 >> 31;
   const uint32_t m0 = (uint32_t)max(S0, -S0), m1 = (uint32_t)max(S1, -S1);
-  const uint32_t lz0 = ffbh(m0), lz1 = ffbh(m1);
-  X0 = (int)(((m0 << (lz0 & 31)) >> 8) << EXTRA) ^ s0;
-  X1 = (int)(((m1 << (lz1 & 31)) >> 8) << EXTRA) ^ s1;
-  const uint32_t lz = __builtin_amdgcn_perm(lz1, lz0, 0x05040100u);  // lz0 | lz1 << 16
+  // lz = lz0 | lz1 << 16; a shift reads the low 5 bits of its amount, so
+  // lz serves as lz0 as it stands and as lz1 through a high-word select
+  const uint32_t lz = ffbh_into_hi(ffbh(m0), m1);
+  X0 = (int)(((m0 << (lz & 31)) >> 8) << EXTRA) ^ s0;
+  X1 = (int)(((m1 << ((lz >> 16) & 31)) >> 8) << EXTRA) ^ s1;
   const u16x2 base = as2(mn) - u16x2{(unsigned short)(31 - F), (unsigned short)(31 - F)};
   NE = as32(__builtin_elementwise_add_sat(as2(lz), base));
 }
