@@ -32,8 +32,9 @@ using namespace fastk;
 
 constexpr int RP = 20;  // LDS row pitch in words: 16-byte aligned b128 rows
 constexpr int EP = 12;  // the same for the 8-word rows of exponent-code pairs
+// (the stage is declared 16-byte aligned for those b128 reads)
 
-struct NStage {
+struct alignas(16) NStage {
   uint32_t av[16][RP];  // [row i][k]
   int as[16][RP];
   uint32_t bv[16][RP];  // [column j][k]
