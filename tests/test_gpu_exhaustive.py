@@ -1,0 +1,87 @@
+"""Every operand code through the GPU kernels, against the oracle.
+
+Row i of A holds code i of the format in slot k = i mod 16, so that every
+FP16 and BF16 code (subnormals, signed zeros, infinities and every NaN
+payload included) is taken in each of the 16 product slots, both Ampere
+stages alike.  "Isolated": the other slots and C hold +0 codes, and every B
+column carries one of the codes below, so D = one product, and each A code
+meets each of those B codes (for E4M3, all 256 codes: every product of two
+codes).  "Embedded": A's other slots, all of B and C are random finite
+values, so each A code's product is summed with 15 others and C.  Each case
+runs on both GEMM kernels and is compared with the oracle bit for bit.
+"""
+import numpy as np
+import pytest
+
+from test_gpu_parity import (assert_bits_equal, gemm_kernel, run_gemm, say,  # noqa: F401
+                             torch_dev)
+
+pytestmark = pytest.mark.gpu
+
+# B codes met by every A code: one, minus one, the largest finite value, the
+# smallest and largest subnormal, the smallest normal, +0, -0, +inf, -inf,
+# a quiet NaN, a value just below two, and a negative mid-range value
+B_CODES = {
+    "fp16": [0x3C00, 0xBC00, 0x7BFF, 0x0001, 0x03FF, 0x0400, 0x0000, 0x8000, 0x7C00, 0xFC00,
+             0x7E00, 0x3FFF, 0xC555],
+    "bf16": [0x3F80, 0xBF80, 0x7F7F, 0x0001, 0x007F, 0x0080, 0x0000, 0x8000, 0x7F80, 0xFF80,
+             0x7FC0, 0x3FFF, 0xC2AA],
+}
+N_RANDOM = 27          # further random B codes: 40 in all (ragged tile edges)
+
+
+def _finite_codes(rng, dt, shape):
+    if dt == "fp16":
+        return rng.standard_normal(shape).astype(np.float16).view(np.uint16)
+    if dt == "bf16":
+        f = rng.standard_normal(shape).astype(np.float32).view(np.uint32)
+        return (f >> 16).astype(np.uint16)
+    c = rng.integers(0, 256, shape, dtype=np.uint16)
+    c[(c & 0x7F) == 0x7F] = 0x38          # E4M3's only NaN codes -> 1.0
+    return c.astype(np.uint8)
+
+
+def _inputs(dt, mode, seed):
+    """A, B and C (None for +0) of one case; row i of A holds code i of the
+    format (all 256 for E4M3) in slot i mod 16."""
+    rng = np.random.default_rng(seed)
+    K = 16
+    cd = np.uint8 if dt == "e4m3" else np.uint16
+    M = 256 if dt == "e4m3" else 65536
+    a_codes = np.arange(M, dtype=np.uint32).astype(cd)
+    if dt == "e4m3":
+        b_row = np.arange(256, dtype=np.uint32).astype(cd)
+    else:
+        extra = rng.integers(0, 65536, N_RANDOM, dtype=np.uint32).astype(cd)
+        b_row = np.concatenate([np.array(B_CODES[dt], cd), extra])
+    nb = len(b_row)
+    if mode == "isolated":
+        # column block k carries the B codes in slot k and +0 elsewhere: in
+        # block (i mod 16) row i's product with each B code is the only term
+        # that is not 0 * 0
+        A = np.zeros((M, K), cd)
+        B = np.zeros((K, K * nb), cd)
+        for k in range(K):
+            B[k, k * nb:(k + 1) * nb] = b_row
+        C = None
+    else:
+        A = _finite_codes(rng, dt, (M, K)).astype(cd)
+        B = _finite_codes(rng, dt, (K, nb)).astype(cd)
+        C = rng.standard_normal((M, nb)).astype(np.float32).view(np.uint32)
+    A[np.arange(M), np.arange(M) % K] = a_codes
+    return A, B, C
+
+
+@pytest.mark.parametrize("mode", ["isolated", "embedded"])
+@pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("hopper", "fp16"),
+                                      ("ampere", "bf16"), ("hopper", "bf16"),
+                                      ("hopper", "e4m3")])
+def test_every_operand_code(torch_dev, orc, gemm_kernel, model, dt, mode):
+    A, B, C = _inputs(dt, mode, 9700 + 10 * ("fp16", "bf16", "e4m3").index(dt)
+                      + (mode == "embedded"))
+    say("every operand code", model, dt, mode, gemm_kernel, A.shape, B.shape)
+    want, wx = orc.gemm(model, dt, A, B, C)
+    got, gx = run_gemm(torch_dev, model, dt, A, B, C)
+    what = f"every {dt} code, {model}, {mode}, {gemm_kernel} kernel"
+    assert_bits_equal(got, want, what)
+    assert_bits_equal(gx, wx, what + " xorsum")
