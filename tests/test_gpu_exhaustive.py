@@ -8,15 +8,31 @@ column carries one of the codes below, so D = one product, and each A code
 meets each of those B codes (for E4M3, all 256 codes: every product of two
 codes).  "Embedded": A's other slots, all of B and C are random finite
 values, so each A code's product is summed with 15 others and C.  Each case
-runs on both GEMM kernels and is compared with the oracle bit for bit.
+runs through all three operand decoders and is compared with the oracle bit
+for bit.
 """
 import numpy as np
 import pytest
 
-from test_gpu_parity import (assert_bits_equal, gemm_kernel, run_gemm, say,  # noqa: F401
-                             torch_dev)
+import os
+
+from test_gpu_parity import assert_bits_equal, run_gemm, say, torch_dev  # noqa: F401
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["tiled", "tiled-in-lds", "narrow"])
+def kernel(request):
+    """The three operand decoders: the tiled kernel's pre-pass (operand
+    images in a workspace), its in-LDS image builder (no workspace; the
+    tile batches use the same builder), and the narrow kernel's own."""
+    env = {"tiled": {"MMAEMU_NARROW_BLOCKS": "0"},
+           "tiled-in-lds": {"MMAEMU_NARROW_BLOCKS": "0", "MMAEMU_NO_WORKSPACE": "1"},
+           "narrow": {"MMAEMU_NARROW_BLOCKS": str(1 << 40)}}[request.param]
+    os.environ.update(env)
+    yield request.param
+    for k in env:
+        del os.environ[k]
 
 # B codes met by every A code: one, minus one, the largest finite value, the
 # smallest and largest subnormal, the smallest normal, +0, -0, +inf, -inf,
@@ -76,12 +92,12 @@ def _inputs(dt, mode, seed):
 @pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("hopper", "fp16"),
                                       ("ampere", "bf16"), ("hopper", "bf16"),
                                       ("hopper", "e4m3")])
-def test_every_operand_code(torch_dev, orc, gemm_kernel, model, dt, mode):
+def test_every_operand_code(torch_dev, orc, kernel, model, dt, mode):
     A, B, C = _inputs(dt, mode, 9700 + 10 * ("fp16", "bf16", "e4m3").index(dt)
                       + (mode == "embedded"))
-    say("every operand code", model, dt, mode, gemm_kernel, A.shape, B.shape)
+    say("every operand code", model, dt, mode, kernel, A.shape, B.shape)
     want, wx = orc.gemm(model, dt, A, B, C)
     got, gx = run_gemm(torch_dev, model, dt, A, B, C)
-    what = f"every {dt} code, {model}, {mode}, {gemm_kernel} kernel"
+    what = f"every {dt} code, {model}, {mode}, {kernel} kernel"
     assert_bits_equal(got, want, what)
     assert_bits_equal(gx, wx, what + " xorsum")
