@@ -6,10 +6,11 @@ payload included) is taken in each of the 16 product slots, both Ampere
 stages alike.  "Isolated": the other slots and C hold +0 codes, and every B
 column carries one of the codes below, so D = one product, and each A code
 meets each of those B codes (for E4M3, all 256 codes: every product of two
-codes).  "Embedded": A's other slots, all of B and C are random finite
-values, so each A code's product is summed with 15 others and C.  Each case
-runs through all three operand decoders and is compared with the oracle bit
-for bit.
+codes).  "Isolated-b" is its mirror image, with every code in B.
+"Embedded": A's other slots, all of B and C are random finite values, so
+each A code's product is summed with 15 others and C.  Each case runs
+through all three operand decoders and is compared with the oracle bit for
+bit.
 """
 import numpy as np
 import pytest
@@ -71,7 +72,7 @@ def _inputs(dt, mode, seed):
         extra = rng.integers(0, 65536, N_RANDOM, dtype=np.uint32).astype(cd)
         b_row = np.concatenate([np.array(B_CODES[dt], cd), extra])
     nb = len(b_row)
-    if mode == "isolated":
+    if mode in ("isolated", "isolated-b"):
         # column block k carries the B codes in slot k and +0 elsewhere: in
         # block (i mod 16) row i's product with each B code is the only term
         # that is not 0 * 0
@@ -85,16 +86,20 @@ def _inputs(dt, mode, seed):
         B = _finite_codes(rng, dt, (K, nb)).astype(cd)
         C = rng.standard_normal((M, nb)).astype(np.float32).view(np.uint32)
     A[np.arange(M), np.arange(M) % K] = a_codes
+    if mode == "isolated-b":
+        # the mirror image: column j of B holds code j in slot j mod 16, and
+        # row block k of A the codes above in slot k
+        A, B = np.ascontiguousarray(B.T), np.ascontiguousarray(A.T)
     return A, B, C
 
 
-@pytest.mark.parametrize("mode", ["isolated", "embedded"])
+@pytest.mark.parametrize("mode", ["isolated", "isolated-b", "embedded"])
 @pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("hopper", "fp16"),
                                       ("ampere", "bf16"), ("hopper", "bf16"),
                                       ("hopper", "e4m3")])
 def test_every_operand_code(torch_dev, orc, kernel, model, dt, mode):
     A, B, C = _inputs(dt, mode, 9700 + 10 * ("fp16", "bf16", "e4m3").index(dt)
-                      + (mode == "embedded"))
+                      + ("isolated", "isolated-b", "embedded").index(mode))
     say("every operand code", model, dt, mode, kernel, A.shape, B.shape)
     want, wx = orc.gemm(model, dt, A, B, C)
     got, gx = run_gemm(torch_dev, model, dt, A, B, C)
