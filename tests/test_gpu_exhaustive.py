@@ -10,7 +10,8 @@ codes).  "Isolated-b" is its mirror image, with every code in B.
 "Embedded": A's other slots, all of B and C are random finite values, so
 each A code's product is summed with 15 others and C.  Each case runs
 through all three operand decoders and is compared with the oracle bit for
-bit.
+bit.  A last test sweeps C the same way: every FP32 exponent field, with
+128 fractions and both signs.
 """
 import numpy as np
 import pytest
@@ -104,5 +105,40 @@ def test_every_operand_code(torch_dev, orc, kernel, model, dt, mode):
     want, wx = orc.gemm(model, dt, A, B, C)
     got, gx = run_gemm(torch_dev, model, dt, A, B, C)
     what = f"every {dt} code, {model}, {mode}, {kernel} kernel"
+    assert_bits_equal(got, want, what)
+    assert_bits_equal(gx, wx, what + " xorsum")
+
+
+def _c_words(rng):
+    """65,536 FP32 words: every exponent field (0 for zeros and subnormals,
+    255 for infinities and NaNs) with 128 fractions each (0, 1, the largest,
+    the top bit alone, and random ones), both signs."""
+    fr = np.concatenate([np.array([0, 1, 0x7FFFFF, 0x400000], np.uint32),
+                         rng.integers(0, 1 << 23, 124, dtype=np.uint32)])
+    e = np.arange(256, dtype=np.uint32)
+    s = np.array([0, 1], np.uint32)
+    w = (s[:, None, None] << 31) | (e[None, :, None] << 23) | fr[None, None, :]
+    return w.reshape(1024, 64)
+
+
+@pytest.mark.parametrize("mode", ["alone", "summed"])
+@pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("hopper", "bf16"),
+                                      ("hopper", "e4m3")])
+def test_every_c_exponent(torch_dev, orc, kernel, model, dt, mode):
+    """C through the state decode and encode: alone (every product 0 * 0),
+    or summed with 16 random finite products."""
+    rng = np.random.default_rng(9800 + ("alone", "summed").index(mode))
+    C = _c_words(rng)
+    M, N, K = C.shape[0], C.shape[1], 16
+    cd = np.uint8 if dt == "e4m3" else np.uint16
+    if mode == "alone":
+        A, B = np.zeros((M, K), cd), np.zeros((K, N), cd)
+    else:
+        A, B = (_finite_codes(rng, dt, (M, K)).astype(cd),
+                _finite_codes(rng, dt, (K, N)).astype(cd))
+    say("every C exponent", model, dt, mode, kernel)
+    want, wx = orc.gemm(model, dt, A, B, C)
+    got, gx = run_gemm(torch_dev, model, dt, A, B, C)
+    what = f"every C exponent, {model}/{dt}, {mode}, {kernel} kernel"
     assert_bits_equal(got, want, what)
     assert_bits_equal(gx, wx, what + " xorsum")
