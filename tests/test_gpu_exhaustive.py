@@ -10,8 +10,8 @@ codes).  "Isolated-b" is its mirror image, with every code in B.
 "Embedded": A's other slots, all of B and C are random finite values, so
 each A code's product is summed with 15 others and C.  Each case runs
 through all three operand decoders and is compared with the oracle bit for
-bit.  A last test sweeps C the same way: every FP32 exponent field, with
-128 fractions and both signs.
+bit.  Two more tests sweep C (every FP32 exponent field, with 128
+fractions and both signs) and take every code through the tile batches.
 """
 import numpy as np
 import pytest
@@ -142,3 +142,36 @@ def test_every_c_exponent(torch_dev, orc, kernel, model, dt, mode):
     what = f"every C exponent, {model}/{dt}, {mode}, {kernel} kernel"
     assert_bits_equal(got, want, what)
     assert_bits_equal(gx, wx, what + " xorsum")
+
+
+@pytest.mark.parametrize("side", ["a", "b"])
+@pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("hopper", "fp16"),
+                                      ("ampere", "bf16"), ("hopper", "bf16"),
+                                      ("hopper", "e4m3")])
+def test_every_operand_code_in_tiles(torch_dev, orc, model, dt, side):
+    """The tile batches: code i of the format sits in tile i // 16 (for E4M3
+    the 256 codes repeat over 16 tiles), row (A) or column (B) i mod 16, at
+    slot (i + i // 16) mod 16; the rest of A and B and all of C are random
+    finite values."""
+    import bit_exact_matrix_amd as mm
+    from test_gpu_parity import to_dev, to_host_bits
+    rng = np.random.default_rng(9900 + 2 * ("fp16", "bf16", "e4m3").index(dt) + (side == "b"))
+    cd = np.uint8 if dt == "e4m3" else np.uint16
+    n = 4096 if dt != "e4m3" else 256
+    codes = np.arange(16 * n, dtype=np.uint32).astype(cd)
+    A = _finite_codes(rng, dt, (n, 16, 16)).astype(cd)
+    B = _finite_codes(rng, dt, (n, 16, 16)).astype(cd)
+    C = rng.standard_normal((n, 16, 16)).astype(np.float32).view(np.uint32)
+    i = np.arange(16 * n)
+    t, r, k = i // 16, i % 16, (i + i // 16) % 16
+    if side == "a":
+        A[t, r, k] = codes
+    else:
+        B[t, k, r] = codes
+    say("every operand code in tiles", model, dt, side)
+    want, wx = orc.tiles(model, dt, A, B, C)
+    D, X = mm.tiles(model, dt, to_dev(torch_dev, A), to_dev(torch_dev, B),
+                    to_dev(torch_dev, C), xorsum=True)
+    what = f"every {dt} code in tiles, {model}, side {side}"
+    assert_bits_equal(to_host_bits(D), want, what)
+    assert_bits_equal(to_host_bits(X), wx, what + " xorsum")
