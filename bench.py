@@ -268,7 +268,7 @@ def bench_tiles(args):
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(1e3 * avg_s, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int32", "data": data,
-        "config": {"workload": args.workload, "tiles": n, "model": model, "input": dtname,
+        "config": {"workload": args.workload, "tiles": n, "mma_model": model, "input": dtname,
                    "accumulator": "fp32", "xorsum": "per-tile", "parallelism": "single-gpu"},
         "bit_exact_vs_oracle": bool(bit_exact), "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3),
@@ -360,6 +360,9 @@ def main():
     for _ in range(args.warmup):
         one()
     torch.cuda.synchronize()
+    # the fingerprint words of the last warm-up launch, to compare with the
+    # timed launches' (the recompute check of the fingerprinting workflow)
+    X_warm = tX.clone() if args.warmup > 0 and not args.verify else None
 
     # timed region: K steps bracketed by synchronisation; HIP events on the
     # launch stream give the per-launch durations (one launch = the operand
@@ -387,6 +390,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    fingerprint_repeats = (bool(torch.equal(tX, X_warm)) if X_warm is not None else None)
     # parity of the timed output against the oracle's full-output digest
     D = tD.cpu().numpy().view(np.uint32)
     X = tX.cpu().numpy().view(np.uint32)
@@ -488,10 +492,11 @@ def main():
         "dtype": "int32",
         "data": data,
         "config": {"workload": args.workload + ("_verify" if args.verify else "") + suffix,
-                   "M": M, "N": N, "K": K, "model": model,
+                   "M": M, "N": N, "K": K, "mma_model": model,
                    "input": dtname, "accumulator": "fp32", "xorsum": "per-row",
                    "parallelism": "single-gpu"},
         "bit_exact_vs_oracle": bool(bit_exact),
+        "fingerprint_repeats": fingerprint_repeats,
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
