@@ -194,7 +194,7 @@ int64_t narrow_blocks() {
 
 // Stream-ordered workspace for the operand pre-pass, from one memory pool
 // per device.  The pool keeps up to the default cap of freed memory cached
-// (its release threshold), so repeated calls do not go back to the driver,
+// (its release threshold), so repeated calls allocate no new device memory,
 // and returns the rest at the next synchronisation.  A failed allocation is
 // not an error: the caller falls back to the kernel that unpacks in place.
 constexpr int kMaxDevices = 64;
