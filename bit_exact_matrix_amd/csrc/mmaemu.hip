@@ -233,6 +233,24 @@ void* workspace_alloc(int64_t bytes, hipStream_t s) {
 template <int MODEL, int DT>
 hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Sink& out,
                        int64_t M, int64_t N, int64_t K, hipStream_t s, int64_t splits = 1) {
+  // A plain chain taller than the tiled grids (65,535 blocks of 64 rows)
+  // runs as row slices of that height: rows of D depend only on the same
+  // rows of A and C, so a slice is the same GEMM on offset pointers.
+  constexpr int64_t kSliceRows = int64_t(65535) * fastk::BM;
+  if (M > kSliceRows && splits == 1 && !out.claimed && !out.accumulate &&
+      gemm_fast_supported(kSliceRows, N, K)) {
+    for (int64_t r0 = 0; r0 < M; r0 += kSliceRows) {
+      const int64_t m = M - r0 < kSliceRows ? M - r0 : kSliceRows;
+      Sink o = out;
+      o.D = out.D + r0 * N;
+      if (out.xorsum) o.xorsum = out.xorsum + r0;
+      const hipError_t e = launch_gemm<MODEL, DT>(
+          (const char*)A + r0 * K * Fmt<DT>::bytes, B, C ? C + r0 * N : nullptr, o, m, N, K,
+          s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  }
   if (out.xorsum && M > 0) {
     const int64_t blocks = (M + 255) / 256;
     fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(out.xorsum, M);

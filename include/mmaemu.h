@@ -56,7 +56,8 @@
  *   kernel with one lane per output, which needs no workspace; the
  *   environment variable MMAEMU_NARROW_BLOCKS sets that threshold in units
  *   of 4096 outputs (0: never), read on every call; shapes over 1,048,560
- *   rows always run on the other kernels.  Either way the results are the
+ *   rows always run on the other kernels.  A plain GEMM over 4,194,240 rows
+ *   runs in row slices of that height.  Either way the results are the
  *   same.
  *   A  M x K row-major raw codes: uint16 (FP16, BF16) or uint8 (E4M3)
  *   B  K x N row-major raw codes, same type

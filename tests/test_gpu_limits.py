@@ -1,12 +1,13 @@
 """Shapes at the library's limits, against the oracle on every output.
 
 * M or N at the tiled kernel's grid limit (65,535 blocks of 64) and one block
-  past it, where the one-lane-per-output reference kernel takes over.  The
-  rows of A and C (or the columns of B and C) repeat with period 61, so that
-  D repeats with period 61 too and the oracle computes only one period; a
-  row or column index that wraps at a power of two lands on a different
-  residue mod 61 and shows.  At the limit the operand images exceed the
-  workspace cap, so those calls also run in chunks of steps.
+  past it: a taller GEMM runs in row slices of that height, a wider one on
+  the one-lane-per-output reference kernel, and so does split-K past the
+  limit.  The rows of A and C (or the columns of B and C) repeat with
+  period 61, so that D repeats with period 61 too and the oracle computes
+  only one period; a row or column index that wraps at a power of two lands
+  on a different residue mod 61 and shows.  At the limit the operand images
+  exceed the workspace cap, so those calls also run in chunks of steps.
 * A long chain: K = 65,536 (4096 chained steps) on one 64 x 64 block.
 """
 import numpy as np
@@ -29,7 +30,7 @@ def _periodic(a, reps, axis):
     return np.tile(a, shape)
 
 
-@pytest.mark.parametrize("rows", [LIMIT, LIMIT + 64])
+@pytest.mark.parametrize("rows", [LIMIT, LIMIT + 64, LIMIT + 1000])
 def test_tall_gemm_at_the_grid_limit(torch_dev, orc, rows):
     N, K = 16, 32
     A0, B, C0 = I.gemm_normal(9300, PERIOD, N, K, I.FP16, c_zero=False)
