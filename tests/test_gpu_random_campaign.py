@@ -2,13 +2,15 @@
 
 Each case draws a model and format (Lovelace included), an input recipe
 (the four adversarial modes, inputs sprinkled with specials, or plain
-normal inputs), a ragged shape up to 299 x 299 x 640, and a path: the tiled
-kernel with its pre-pass, the tiled kernel building its images in LDS, the
-narrow kernel, the split-K schedule (a random divisor of the step count),
+normal inputs), a ragged shape (by default up to 299 x 299 x 640), and a
+path: the tiled kernel with its pre-pass, the tiled kernel building its
+images in LDS, the narrow kernel, the split-K schedule (a random divisor of the step count),
 the audit compare (0 to 4 planted bit flips), or a batch of up to 1999
 independent tiles.  Every output word, fingerprint and report must equal
 the oracle's.  MMAEMU_CAMPAIGN_CASES sets the number of cases (2000 by
-default; a run of 25,000 took about 4.5 minutes on one MI355X).
+default; a run of 25,000 took about 4.5 minutes on one MI355X), and
+MMAEMU_CAMPAIGN_MAX_MN and MMAEMU_CAMPAIGN_MAX_STEPS the shape bounds (300
+and 40 by default).
 """
 import os
 
@@ -26,6 +28,9 @@ COMBOS = [("ampere", "fp16"), ("hopper", "fp16"), ("ampere", "bf16"), ("hopper",
 RECIPES = ["wide", "narrow", "coarse", "tiny", "specials", "normal"]
 PATHS = ["tiled", "tiled-in-lds", "narrow", "splitk", "verify", "tiles"]
 ENV = ("MMAEMU_NARROW_BLOCKS", "MMAEMU_NO_WORKSPACE")
+# shape bounds: M, N below MAX_MN, K up to 16 * MAX_STEPS
+MAX_MN = int(os.environ.get("MMAEMU_CAMPAIGN_MAX_MN", "300"))
+MAX_STEPS = int(os.environ.get("MMAEMU_CAMPAIGN_MAX_STEPS", "40"))
 
 
 def _set_path(path):
@@ -62,8 +67,8 @@ def _one_case(torch_dev, orc, case):
     model, dt = COMBOS[rng.integers(len(COMBOS))]
     recipe = RECIPES[rng.integers(len(RECIPES))]
     path = PATHS[rng.integers(len(PATHS))]
-    M, N = int(rng.integers(1, 300)), int(rng.integers(1, 300))
-    T = int(rng.integers(1, 41))
+    M, N = int(rng.integers(1, MAX_MN)), int(rng.integers(1, MAX_MN))
+    T = int(rng.integers(1, MAX_STEPS + 1))
     K = 16 * T
     seed = 2_000_000 + case
     _set_path(path)
