@@ -4,10 +4,10 @@ Each case draws a model and format (Lovelace included), an input recipe
 (the four adversarial modes, inputs sprinkled with specials, or plain
 normal inputs), a ragged shape (by default up to 299 x 299 x 640), and a
 path: the tiled kernel with its pre-pass, the tiled kernel building its
-images in LDS, the narrow kernel, the split-K schedule (a random divisor of the step count),
-the audit compare (0 to 4 planted bit flips), or a batch of up to 1999
-independent tiles.  Every output word, fingerprint and report must equal
-the oracle's.  MMAEMU_CAMPAIGN_CASES sets the number of cases (2000 by
+images in LDS, the narrow kernel, the split-K schedule (a random divisor of
+the step count), the audit compare (0 to 4 planted bit flips), or a batch
+of up to 1999 independent tiles.  Every output word, fingerprint and
+report must equal the oracle's.  MMAEMU_CAMPAIGN_CASES sets the number of cases (2000 by
 default; a run of 25,000 took about 4.5 minutes on one MI355X), and
 MMAEMU_CAMPAIGN_MAX_MN and MMAEMU_CAMPAIGN_MAX_STEPS the shape bounds (300
 and 40 by default).
