@@ -268,7 +268,7 @@ __device__ __forceinline__ void produce(ST* st, const uint32_t (&ca)[4],
   // B exponents: k paired with the adjacent lane
   uint32_t pb[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) pb[u] = __shfl_xor(bne[u], 1, 64);
+  for (int u = 0; u < 4; ++u) pb[u] = from_lane_xor1(bne[u]);
   if ((k & 1) == 0) {
     *(uint4*)&st->b.ne[k >> 1][4 * q] =
         make_uint4(bne[0] | pb[0] << 16, bne[1] | pb[1] << 16, bne[2] | pb[2] << 16,
@@ -392,7 +392,7 @@ __global__ __launch_bounds__(64) void unpack_kernel(const void* __restrict__ src
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const uint32_t mine = (r & 1) ? ne[2 * p + 1] : ne[2 * p];
-      const uint32_t other = __shfl_xor((r & 1) ? ne[2 * p] : ne[2 * p + 1], 1, 64);
+      const uint32_t other = from_lane_xor1((r & 1) ? ne[2 * p] : ne[2 * p + 1]);
       img->ne[p][r] = (r & 1) ? (other | mine << 16) : (mine | other << 16);
     }
   }

@@ -249,6 +249,20 @@ __device__ __forceinline__ uint32_t load_code(const void* p, int64_t idx) {
   return ((const uint16_t*)p)[idx];
 }
 
+// x from the lane whose index differs in bit 0: a DPP quad permutation
+// [1, 0, 3, 2], a VALU move that needs every lane of the wave active.
+__device__ __forceinline__ uint32_t from_lane_xor1(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
+}
+// The XOR of x over each row of 16 lanes, in every lane of the row: DPP row
+// rotations by 8, 4, 2 and 1 (every lane of the wave active).
+__device__ __forceinline__ uint32_t row16_xor(uint32_t x) {
+  x ^= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x128, 0xF, 0xF, false);  // row_ror:8
+  x ^= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x124, 0xF, 0xF, false);  // row_ror:4
+  x ^= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x122, 0xF, 0xF, false);  // row_ror:2
+  x ^= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x121, 0xF, 0xF, false);  // row_ror:1
+  return x;
+}
 // XOR of a value over the 64 lanes of a wavefront (order-free: XOR is
 // exactly associative and commutative).
 __device__ __forceinline__ uint32_t wave_xor(uint32_t v) {

@@ -177,8 +177,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void ti
     }
     if (xorsum) {
       // the tile's 256 words: XOR over the 16 lanes of tile u
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) xs ^= __shfl_xor(xs, off, 16);
+      xs = row16_xor(xs);
       if ((lane & 15) == 0 && live) xorsum[tile] = xs;
     }
   }
