@@ -2,14 +2,15 @@
 (bit_exact_matrix_amd/probe/valu_rate.hip) runs dependency chains of one
 instruction at a time.  The instructions that carry the hot loop's per-MAC
 work (exact product, sign-and-accumulate, the packed exponent add and
-maximum, the word-select shift) and its normalisation must issue at the
-peak derived from the unit counts and the clock (one wave64 instruction per
-SIMD every 4 cycles), within a few per cent, and never above it.  A few
-simple 32-bit operations issue faster on gfx950; for them only the lower
-bound is checked.  The hot loop's own pass-2 mix (exact products,
+maximum, the word-select shift) and its normalisation must never issue
+above the peak derived from the unit counts and the clock (one wave64
+instruction per SIMD every 4 cycles); on one MI355X they reach 0.92 to 0.98
+of it.  Every probe must reach 0.75 of it, a floor that only a broken probe
+misses.  A few simple 32-bit operations issue faster on gfx950; for them
+only that floor is checked.  The hot loop's own pass-2 mix (exact products,
 alignment shifts, one of them from a high word, sign-and-accumulates and
-the packed distance add) must issue at the derived peak too, within 10%:
-the faster simple operations do not lift this mix's ceiling."""
+the packed distance add) must stay within 1.1 times the derived peak: the
+faster simple operations do not lift this mix's ceiling."""
 import ctypes
 import os
 
@@ -43,7 +44,9 @@ def test_issue_rates_against_the_derived_peak(torch_dev):
         name = lib.valu_rate_name(op).decode()
         seen.add(name)
         say("VALU issue rate", name, f"{rate / 1e12:.2f}e12 lane-op/s", f"{rate / PEAK:.3f} of peak")
-        assert rate >= 0.9 * PEAK, f"{name} reaches only {rate / PEAK:.2f} of the peak"
+        # a floor that only a broken probe misses: a box held below the
+        # 2.4 GHz clock must not fail the suite (measured: 0.92 .. 0.98)
+        assert rate >= 0.75 * PEAK, f"{name} reaches only {rate / PEAK:.2f} of the peak"
         if name in AT_PEAK:
             assert rate <= 1.02 * PEAK, f"{name} runs above the derived peak: {rate:.3e}"
         if name == MIX:
