@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
       image_a<MODEL, DT>(ca, v, s, ne);
       st->av[i][j] = v;
       st->as[i][j] = s;
-      const uint32_t ne_a1 = __shfl_xor(ne, 1, 64);  // the same row's code at k ^ 1
+      const uint32_t ne_a1 = from_lane_xor1(ne);  // the same row's code at k ^ 1
       if ((j & 1) == 0) st->ae[i][j >> 1] = ne | ne_a1 << 16;
       const uint64_t bal_a = __ballot(s != 0);       // bit 16*(i&3) + k: row i's signs
       if (j == 0) st->am[i] = (uint32_t)(bal_a >> (16 * (i & 3))) & 0xFFFFu;
@@ -152,7 +152,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
       image_b<DT>(cb, v, s, ne);
       st->bv[j][i] = v;
       st->bs[j][i] = s;
-      const uint32_t ne_b1 = __shfl_xor(ne, 16, 64);  // the same column's code at k ^ 1
+      // the same column's code at k ^ 1, for the even rows i that use it
+      const uint32_t ne_b1 = from_next_row16(ne);
       if ((i & 1) == 0) st->be[j][i >> 1] = ne | ne_b1 << 16;
       // column j's signs at k = 4*wv + r sit in bits 16*r + j of this wave's ballot
       const uint64_t bal_b = __ballot(s != 0);

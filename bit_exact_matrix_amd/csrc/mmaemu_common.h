@@ -254,6 +254,12 @@ __device__ __forceinline__ uint32_t load_code(const void* p, int64_t idx) {
 __device__ __forceinline__ uint32_t from_lane_xor1(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);
 }
+// In each even row of 16 lanes (lanes 0-15 and 32-47), x from the row
+// after it; odd rows get their own x back.  One v_permlane16_swap (every
+// lane of the wave active).
+__device__ __forceinline__ uint32_t from_next_row16(uint32_t x) {
+  return __builtin_amdgcn_permlane16_swap(x, x, false, false)[1];
+}
 // The XOR of x over each row of 16 lanes, in every lane of the row: DPP row
 // rotations by 8, 4, 2 and 1 (every lane of the wave active).
 __device__ __forceinline__ uint32_t row16_xor(uint32_t x) {
