@@ -174,14 +174,28 @@ int64_t workspace_cap() {
   return kDefaultWorkspaceCap;
 }
 
-// Below this many 64x64 blocks' worth of outputs (M*N / 4096) the tiled
-// kernel, whose lanes hold 4x4 outputs each, cannot fill the chip, and a
-// plain chain runs on the narrow kernel (one lane per output) instead.
-// Measured on one MI355X: the narrow kernel is 2.3x faster at 64 blocks and
-// 1.3x at 128, the tiled one 1.4x faster at 256.  MMAEMU_NARROW_BLOCKS
-// overrides the threshold (0: never), read on every call.
-constexpr int64_t kNarrowBlocks = 192;
+// Which chain kernel is faster for an M x N output: an estimate of each
+// one's time per K-step (both scale with the step count), in units of
+// 10 ns, fitted on one MI355X (FP16 Ampere and E4M3 Hopper, 18 shapes from
+// 1 x 4096 to 2048 x 256 and 1024 x 1024, K from 1024 to 65536):
+//  * narrow kernel, one lane per output in 16 x 16 tiles:
+//    max(0.74, 0.44 + 0.0013 * tiles) us, a latency floor for small shapes;
+//  * tiled kernel, 4 x 4 outputs per lane in 64 x 64 blocks: 4.45 us per
+//    round of 256 blocks (one per CU) up to 1024 blocks, 2.7 us per 256
+//    blocks beyond (three at a time per CU).
+// A few rows against a wide N (a decoding step) go to the narrow kernel
+// even when M * N is large: the tiled kernel pays for whole 64-row blocks.
+bool narrow_is_faster(int64_t M, int64_t N) {
+  const int64_t t16 = ((M + 15) / 16) * ((N + 15) / 16);
+  const int64_t b64 = ((M + 63) / 64) * ((N + 63) / 64);
+  const int64_t narrow = 44 + t16 * 13 / 100 > 74 ? 44 + t16 * 13 / 100 : 74;
+  const int64_t tiled = b64 <= 1024 ? 445 * ((b64 + 255) / 256) : 270 * b64 / 256;
+  return narrow < tiled;
+}
 
+// MMAEMU_NARROW_BLOCKS, read on every call, replaces that estimate by a
+// threshold: the narrow kernel below that many 64 x 64 blocks' worth of
+// outputs (M * N / 4096), 0 never.  -1 when it is not set.
 int64_t narrow_blocks() {
   const char* v = getenv("MMAEMU_NARROW_BLOCKS");
   if (v && *v) {
@@ -189,7 +203,7 @@ int64_t narrow_blocks() {
     const long long x = strtoll(v, &end, 10);
     if (end && *end == '\0' && x >= 0) return (int64_t)x;
   }
-  return kNarrowBlocks;
+  return -1;
 }
 
 // Stream-ordered workspace for the operand pre-pass, from one memory pool
@@ -259,8 +273,9 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
   if (M == 0 || N == 0) return hipGetLastError();
   // (the narrow grid's y dimension, 16 rows a block, stays within 65,535
   // blocks, as the tiled grid's does; a taller shape runs tiled)
+  const int64_t nb_env = narrow_blocks();
   if (gemm_fast_supported(M, N, K) && splits == 1 && (M + 15) / 16 <= 65535 &&
-      M * N / 4096 < narrow_blocks()) {
+      (nb_env >= 0 ? M * N / 4096 < nb_env : narrow_is_faster(M, N))) {
     narrowk::gemm_narrow_kernel<MODEL, DT>
         <<<dim3((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), dim3(256), 0, s>>>(
             A, B, C, out, M, N, K, 0, K / 16);

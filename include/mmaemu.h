@@ -52,11 +52,13 @@
  *   environment variable MMAEMU_NO_WORKSPACE is set, the call stages the
  *   operands in LDS instead (same results, slower) and allocates nothing.
  *   mma_emulate_tiles allocates nothing.  No other state is kept between
- *   calls.  GEMMs with fewer than 192 x 4096 outputs (M * N) run on a
- *   kernel with one lane per output, which needs no workspace; the
- *   environment variable MMAEMU_NARROW_BLOCKS sets that threshold in units
- *   of 4096 outputs (0: never), read on every call; shapes over 1,048,560
- *   rows always run on the other kernels.  A plain GEMM over 4,194,240 rows
+ *   calls.  A plain chain runs on a kernel with one lane per output, which
+ *   needs no workspace, when an estimate of both kernels' time says it is
+ *   the faster (small M * N, or a few rows against a wide N); setting the
+ *   environment variable MMAEMU_NARROW_BLOCKS replaces that estimate by a
+ *   threshold: that kernel below that many units of 4096 outputs (M * N),
+ *   0 never; read on every call.  Shapes over 1,048,560 rows always run on
+ *   the other kernels.  A plain GEMM over 4,194,240 rows
  *   runs in row slices of that height.  Either way the results are the
  *   same.
  *   A  M x K row-major raw codes: uint16 (FP16, BF16) or uint8 (E4M3)

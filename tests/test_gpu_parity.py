@@ -252,9 +252,9 @@ def no_workspace():
 def gemm_kernel(request):
     """Run a test once on each GEMM kernel: the tiled one (4x4 outputs per
     lane) and the narrow one (one output per lane), which the library takes
-    for plain chains with few 64x64 blocks.  MMAEMU_NARROW_BLOCKS is the
-    block-count threshold: 0 never takes the narrow kernel, a huge value
-    always (where it applies)."""
+    for plain chains where it estimates it the faster.  MMAEMU_NARROW_BLOCKS
+    replaces the estimate by a block-count threshold: 0 never takes the
+    narrow kernel, a huge value always (where it applies)."""
     os.environ["MMAEMU_NARROW_BLOCKS"] = "0" if request.param == "tiled" else str(1 << 40)
     yield request.param
     del os.environ["MMAEMU_NARROW_BLOCKS"]
