@@ -58,9 +58,8 @@
  *   environment variable MMAEMU_NARROW_BLOCKS replaces that estimate by a
  *   threshold: that kernel below that many units of 4096 outputs (M * N),
  *   0 never; read on every call.  Shapes over 1,048,560 rows always run on
- *   the other kernels.  A plain GEMM over 4,194,240 rows
- *   runs in row slices of that height.  Either way the results are the
- *   same.
+ *   the other kernels, and a plain GEMM over 4,194,240 rows runs in row
+ *   slices of that height.  Either way the results are the same.
  *   A  M x K row-major raw codes: uint16 (FP16, BF16) or uint8 (E4M3)
  *   B  K x N row-major raw codes, same type
  *   C  M x N row-major FP32 (read as bit patterns); NULL means all +0.0
