@@ -10,7 +10,8 @@ of up to 1999 independent tiles.  Every output word, fingerprint and
 report must equal the oracle's.  MMAEMU_CAMPAIGN_CASES sets the number of cases (2000 by
 default; a run of 25,000 took about 4.5 minutes on one MI355X), and
 MMAEMU_CAMPAIGN_MAX_MN and MMAEMU_CAMPAIGN_MAX_STEPS the shape bounds (300
-and 40 by default).
+and 40 by default); MMAEMU_CAMPAIGN_FIRST starts at another case index, so
+that a long run can cover cases no earlier run drew.
 """
 import os
 
@@ -109,15 +110,16 @@ def _one_case(torch_dev, orc, case):
 
 def test_random_campaign(torch_dev, orc):
     n = int(os.environ.get("MMAEMU_CAMPAIGN_CASES", "2000"))
+    first = int(os.environ.get("MMAEMU_CAMPAIGN_FIRST", "0"))
     failures = []
     try:
-        for case in range(n):
+        for case in range(first, first + n):
             bad = _one_case(torch_dev, orc, case)
             if bad:
                 failures.append(bad)
                 say("campaign: differs from the oracle:", bad)
-            if case % 500 == 499:
-                say(f"campaign: {case + 1} of {n} cases, {len(failures)} differ")
+            if (case - first) % 500 == 499:
+                say(f"campaign: {case - first + 1} of {n} cases, {len(failures)} differ")
     finally:
         for k in ENV:
             os.environ.pop(k, None)
