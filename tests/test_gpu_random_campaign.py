@@ -14,6 +14,7 @@ and 40 by default); MMAEMU_CAMPAIGN_FIRST starts at another case index, so
 that a long run can cover cases no earlier run drew.
 """
 import os
+import time
 
 import numpy as np
 import pytest
@@ -112,14 +113,17 @@ def test_random_campaign(torch_dev, orc):
     n = int(os.environ.get("MMAEMU_CAMPAIGN_CASES", "2000"))
     first = int(os.environ.get("MMAEMU_CAMPAIGN_FIRST", "0"))
     failures = []
+    last = time.monotonic()
     try:
         for case in range(first, first + n):
             bad = _one_case(torch_dev, orc, case)
             if bad:
                 failures.append(bad)
                 say("campaign: differs from the oracle:", bad)
-            if (case - first) % 500 == 499:
+            # a progress line every 500 cases or 30 s, whichever comes first
+            if (case - first) % 500 == 499 or time.monotonic() - last > 30:
                 say(f"campaign: {case - first + 1} of {n} cases, {len(failures)} differ")
+                last = time.monotonic()
     finally:
         for k in ENV:
             os.environ.pop(k, None)
