@@ -24,14 +24,15 @@
  *  R3  Product.  s = sa^sb, E = Ea+Eb, m = ma*mb, f = fa+fb: exact and not
  *      normalised ("Key observation 1": (2^11-1)^2 survives exactly;
  *      "Key observation 3" and the Target Tests table: delayed normalisation;
- *      pipeline: product kept at extended precision, mraw<<3).
+ *      pipeline: the raw product is kept wide and widened by three bits).
  *  R4  GroupSum_F over a list of terms.  Zero terms take no part in the max
  *      search (reading, from the neutral-subgroup test of the Core method:
  *      zeroed terms behave as absent).  emax = max E over non-zero terms.
  *      Each term is put on the grid 2^(emax-F): M = m*2^(F-f), then its
  *      MAGNITUDE is shifted right by emax-E with truncation (Target Tests:
- *      round towards zero at alignment; pipeline: mi >> delta-e), then the
- *      sign is applied and the exact integer sum S is formed.
+ *      round towards zero at alignment; pipeline: a right shift by the
+ *      exponent difference), then the sign is applied and the exact integer
+ *      sum S is formed.
  *      F = 23 for Ampere (24-bit internal significand incl. the implicit
  *      bit), F = 24 for Hopper (25 bits) ("Key observation 3").
  *  R5  Norm_W.  n = bitlen|S|, exponent L = emax-F+n-1 (unbounded: BF16
