@@ -111,6 +111,11 @@ def parse():
     p.add_argument("--valu-peak", action="store_true",
                    help="instead of a workload, measure the issue rate of the hot loop's "
                         "VALU instructions (libvalurate.so) against the derived peak")
+    p.add_argument("--shape", default=None,
+                   help="instead of a workload, time one GEMM of this shape, MxNxK, with "
+                        "seeded inputs; sampled rows are checked against the oracle")
+    p.add_argument("--mma", default="ampere/fp16",
+                   help="model/format for --shape (ampere|hopper|lovelace / fp16|bf16|e4m3)")
     p.add_argument("--copy-calibration", action="store_true",
                    help="after the timed region, run a plain 256 MiB device copy twice "
                         "(reference kernel for scaling HBM byte counters)")
@@ -155,6 +160,77 @@ def bench_valu_peak(args):
         "peak_derived": VALU_PEAK_OPS,
         "rates": {k: round(v, 1) for k, v in rates.items()},
         "frac_of_derived_peak": {k: round(v / VALU_PEAK_OPS, 4) for k, v in rates.items()},
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_shape(args):
+    """One GEMM of any shape (--shape MxNxK, --mma model/format): A, B ~N(0,1)
+    (E4M3: uniform over the finite codes), C = +0, seed M + N + K.  The
+    library picks the kernel unless MMAEMU_NARROW_BLOCKS forces one.  Rows
+    first, middle and last of D are recomputed with the oracle afterwards and
+    compared bit for bit (bit_exact_sampled_rows)."""
+    import numpy as np
+    import torch
+
+    import bit_exact_matrix_amd as mm
+    import oracle
+    from bit_exact_matrix_amd import inputs as I
+
+    try:
+        M, N, K = (int(x) for x in args.shape.lower().split("x"))
+        model, dtname = args.mma.lower().split("/")
+        if (M < 1 or N < 1 or K < 16 or K % 16 or model not in mm.MODELS
+                or dtname not in ("fp16", "bf16", "e4m3")):
+            raise ValueError
+    except ValueError:
+        print("--shape takes MxNxK (M, N >= 1, K a positive multiple of 16) and --mma "
+              "model/format", file=sys.stderr)
+        sys.exit(2)
+    seed = M + N + K
+    if dtname == "e4m3":
+        A, B, _ = I.gemm_e4m3(seed, M, N, K)
+    else:
+        A, B, _ = I.gemm_normal(seed, M, N, K, I.FP16 if dtname == "fp16" else I.BF16)
+    mm.load_library()
+    dev = torch.device("cuda:0")
+    code_t = np.int8 if dtname == "e4m3" else np.int16
+    tA = torch.from_numpy(A.view(code_t)).to(dev)
+    tB = torch.from_numpy(B.view(code_t)).to(dev)
+    D, X = mm.gemm(model, dtname, tA, tB, None, xorsum=True)
+    for _ in range(args.warmup):
+        mm.gemm(model, dtname, tA, tB, None, D=D, xorsum=True)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        mm.gemm(model, dtname, tA, tB, None, D=D, xorsum=True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    got = D.cpu().numpy().view(np.uint32)
+    ok = True
+    for r in sorted({0, M // 2, M - 1}):
+        want, _ = oracle.gemm_rows(model, dtname, A, B, None, r, r + 1)
+        ok &= bool(np.array_equal(got[r:r + 1], want))
+    macs = M * N * K
+    alg = ALG_SLOTS_PER_MAC["hopper" if model == "hopper" else "ampere"]
+    out = {
+        "metric": f"bit-exact emulated MACs/s, {M}x{N}x{K} {dtname.upper()} "
+                  f"{model.capitalize()} model",
+        "value": round(macs / (ms / 1e3), 1), "unit": "MAC/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int32", "data": f"synthetic: seed {seed}, C = +0",
+        "config": {"workload": f"gemm_{M}x{N}x{K}_{dtname}_{model}", "M": M, "N": N, "K": K,
+                   "mma_model": model, "input": dtname,
+                   "kernel_override": os.environ.get("MMAEMU_NARROW_BLOCKS")},
+        "bit_exact_sampled_rows": ok,
+        "roofline": {"bound": "alu", "achieved": round(alg * macs / (ms / 1e3) / 1e12, 3),
+                     "peak": round(VALU_PEAK_OPS / 1e12, 3), "unit": "TOP/s",
+                     "frac": round(alg * macs / (ms / 1e3) / VALU_PEAK_OPS, 4)},
+        "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
 
@@ -292,6 +368,8 @@ def main():
         sys.exit(2)
     if args.valu_peak:
         return bench_valu_peak(args)
+    if args.shape:
+        return bench_shape(args)
     if args.workload in TILE_WORKLOADS:
         if args.verify or args.splits != 1:
             print("--verify and --splits apply to the GEMM workloads", file=sys.stderr)
