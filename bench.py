@@ -165,11 +165,12 @@ def bench_valu_peak(args):
 
 
 def bench_shape(args):
-    """One GEMM of any shape (--shape MxNxK, --mma model/format): A, B ~N(0,1)
-    (E4M3: uniform over the finite codes), C = +0, seed M + N + K.  The
-    library picks the kernel unless MMAEMU_NARROW_BLOCKS forces one.  Rows
-    first, middle and last of D are recomputed with the oracle afterwards and
-    compared bit for bit (bit_exact_sampled_rows)."""
+    """One GEMM of any shape (--shape MxNxK, --mma model/format, --splits for
+    the split-K schedule): A, B ~N(0,1) (E4M3: uniform over the finite
+    codes), C = +0, seed M + N + K.  The library picks the kernel unless
+    MMAEMU_NARROW_BLOCKS forces one.  Rows first, middle and last of D are
+    recomputed with the oracle afterwards and compared bit for bit
+    (bit_exact_sampled_rows)."""
     import numpy as np
     import torch
 
@@ -181,11 +182,12 @@ def bench_shape(args):
         M, N, K = (int(x) for x in args.shape.lower().split("x"))
         model, dtname = args.mma.lower().split("/")
         if (M < 1 or N < 1 or K < 16 or K % 16 or model not in mm.MODELS
-                or dtname not in ("fp16", "bf16", "e4m3")):
+                or dtname not in ("fp16", "bf16", "e4m3") or args.splits < 1
+                or (K // 16) % args.splits):
             raise ValueError
     except ValueError:
         print("--shape takes MxNxK (M, N >= 1, K a positive multiple of 16) and --mma "
-              "model/format", file=sys.stderr)
+              "model/format; --splits must divide K/16", file=sys.stderr)
         sys.exit(2)
     seed = M + N + K
     if dtname == "e4m3":
@@ -197,34 +199,38 @@ def bench_shape(args):
     code_t = np.int8 if dtname == "e4m3" else np.int16
     tA = torch.from_numpy(A.view(code_t)).to(dev)
     tB = torch.from_numpy(B.view(code_t)).to(dev)
-    D, X = mm.gemm(model, dtname, tA, tB, None, xorsum=True)
+    sp = args.splits
+    D, X = mm.gemm(model, dtname, tA, tB, None, xorsum=True, splits=sp)
     for _ in range(args.warmup):
-        mm.gemm(model, dtname, tA, tB, None, D=D, xorsum=True)
+        mm.gemm(model, dtname, tA, tB, None, D=D, xorsum=True, splits=sp)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
-        mm.gemm(model, dtname, tA, tB, None, D=D, xorsum=True)
+        mm.gemm(model, dtname, tA, tB, None, D=D, xorsum=True, splits=sp)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     got = D.cpu().numpy().view(np.uint32)
     ok = True
     for r in sorted({0, M // 2, M - 1}):
-        want, _ = oracle.gemm_rows(model, dtname, A, B, None, r, r + 1)
+        if sp > 1:
+            want, _ = oracle.gemm_splitk(model, dtname, A[r:r + 1], B, None, sp)
+        else:
+            want, _ = oracle.gemm_rows(model, dtname, A, B, None, r, r + 1)
         ok &= bool(np.array_equal(got[r:r + 1], want))
     macs = M * N * K
     alg = ALG_SLOTS_PER_MAC["hopper" if model == "hopper" else "ampere"]
     out = {
         "metric": f"bit-exact emulated MACs/s, {M}x{N}x{K} {dtname.upper()} "
-                  f"{model.capitalize()} model",
+                  f"{model.capitalize()} model" + (f", split-K {sp}" if sp > 1 else ""),
         "value": round(macs / (ms / 1e3), 1), "unit": "MAC/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "int32", "data": f"synthetic: seed {seed}, C = +0",
         "config": {"workload": f"gemm_{M}x{N}x{K}_{dtname}_{model}", "M": M, "N": N, "K": K,
-                   "mma_model": model, "input": dtname,
+                   "mma_model": model, "input": dtname, "splits": sp,
                    "kernel_override": os.environ.get("MMAEMU_NARROW_BLOCKS")},
         "bit_exact_sampled_rows": ok,
         "roofline": {"bound": "alu", "achieved": round(alg * macs / (ms / 1e3) / 1e12, 3),

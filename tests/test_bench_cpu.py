@@ -49,9 +49,9 @@ def test_every_tile_workload_has_a_stored_digest():
 def test_shape_mode_rejects_bad_shapes_before_touching_a_gpu():
     for shape, mma in (("10x10x15", "ampere/fp16"), ("0x16x16", "ampere/fp16"),
                        ("16x16", "ampere/fp16"), ("16x16x16", "volta/fp16"),
-                       ("16x16x16", "ampere/fp32")):
+                       ("16x16x16", "ampere/fp32"), ("16x16x48", "ampere/fp16 --splits 2")):
         r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--shape", shape,
-                            "--mma", mma], capture_output=True, text=True, timeout=120)
+                            "--mma", *mma.split()], capture_output=True, text=True, timeout=120)
         assert r.returncode == 2, (shape, mma, r.stderr[-300:])
         assert "--shape takes MxNxK" in r.stderr
         assert r.stdout == ""
