@@ -148,6 +148,38 @@ def gemm_splitk(model, dtype, A, B, C, splits, nthreads=0, lib=None):
     return acc, x
 
 
+def step_sequence(order, T):
+    """The step that each position of the chain applies: position s takes
+    step order[s], read as an unsigned 32-bit integer and clamped to T - 1
+    (reading: the order is a model input that the pages leave open; a
+    permutation of 0..T-1 is the intended use, and the clamp gives every
+    other sequence of T words a defined meaning)."""
+    order = np.asarray(order)
+    assert order.shape == (T,), f"an order needs one entry per K-step ({T})"
+    return np.minimum(order.astype(np.int64) & 0xFFFFFFFF, T - 1)
+
+
+def gemm_ordered(model, dtype, A, B, C, order, nthreads=0, lib=None, rows=None):
+    """The chained GEMM with its K-steps taken in a given order: C_0 = C,
+    C_{s+1} = one MMA step of C_s with step t = order[s] of A and B (the
+    16 columns A[:, 16t..16t+15] and rows B[16t..16t+15, :]), D = C_T for
+    the T = K/16 steps.  The pages leave the order in which a library walks
+    K open, as a schedule still to be characterised (Hawkeye notes,
+    "Critical Analysis" and Future work 4); the forward order 0, 1, .., T-1
+    is the plain gemm.  Written as the plain gemm on A and B with their
+    K-blocks gathered in that order.  rows = (r0, r1) computes rows
+    [r0, r1) only.  Returns (D bits, per-row xorsum)."""
+    M, K = A.shape
+    steps = step_sequence(order, K // 16)
+    cols = (16 * steps[:, None] + np.arange(16)[None, :]).reshape(-1)
+    if rows is not None:
+        r0, r1 = rows
+        A = A[r0:r1]
+        C = None if C is None else C[r0:r1]
+    return gemm(model, dtype, np.ascontiguousarray(A[:, cols]),
+                np.ascontiguousarray(B[cols, :]), C, nthreads=nthreads, lib=lib)
+
+
 def compare(D, D_claimed):
     """Bitwise comparison of an emulated D with a claimed one (both M x N
     bit patterns): (number of differing elements, smallest differing

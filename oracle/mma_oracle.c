@@ -69,9 +69,11 @@
  *      parameter that tells them apart, so no difference is modelled.  FP8
  *      E4M3 stays Hopper-only.
  */
+#define _GNU_SOURCE /* sched_getaffinity */
 #include "mma_oracle.h"
 
 #include <pthread.h>
+#include <sched.h>
 #include <stdlib.h>
 #include <string.h>
 #include <unistd.h>
@@ -339,8 +341,14 @@ static uint32_t load_code(const void *p, int dtype, int64_t idx) {
   return ((const uint16_t *)p)[idx];
 }
 
+/* The CPUs this process may run on (its affinity mask, which a container's
+ * or a scheduler's CPU set narrows), else the online count. */
 int mma_oracle_num_cpus(void) {
-  long n = sysconf(_SC_NPROCESSORS_ONLN);
+  cpu_set_t set;
+  long n;
+  if (sched_getaffinity(0, sizeof set, &set) == 0 && CPU_COUNT(&set) > 0)
+    return CPU_COUNT(&set);
+  n = sysconf(_SC_NPROCESSORS_ONLN);
   return n > 0 ? (int)n : 1;
 }
 

@@ -49,7 +49,8 @@ def inputs_sha256(A, B, C):
 
 def workloads():
     """name -> (kind, model, dtype, generator) for the five seeded configs
-    (and the 4096^3 FP16 Ampere GEMM under the 4-run split-K schedule)."""
+    (and the 4096^3 FP16 Ampere GEMM under the 4-run split-K schedule and
+    with its 256 K-steps in reversed order)."""
     return {
         "tiles_fp16_1k_ampere": ("tiles", "ampere", "fp16", lambda: I.tiles_normal(1001, 1000)),
         "tiles_mixed_100k_fp16_ampere": ("tiles", "ampere", "fp16",
@@ -68,6 +69,8 @@ def workloads():
                                   lambda: I.gemm_e4m3(5001, 4096, 4096, 4096)),
         "gemm_4096_fp16_ampere_splitk4": ("splitk4", "ampere", "fp16",
                                           lambda: I.gemm_normal(3001, 4096, 4096, 4096)),
+        "gemm_4096_fp16_ampere_reversed": ("reversed", "ampere", "fp16",
+                                           lambda: I.gemm_normal(3001, 4096, 4096, 4096)),
     }
 
 
@@ -83,6 +86,9 @@ def main(names):
             D, x = oracle.tiles(model, dt, A, B, C)
         elif kind == "splitk4":
             D, x = oracle.gemm_splitk(model, dt, A, B, C, 4)
+        elif kind == "reversed":
+            T = A.shape[1] // 16
+            D, x = oracle.gemm_ordered(model, dt, A, B, C, np.arange(T - 1, -1, -1, dtype=np.int32))
         else:
             D, x = oracle.gemm(model, dt, A, B, C)
         dt_s = time.time() - t
