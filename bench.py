@@ -10,7 +10,8 @@ same size instead.  --verify times the audit compare (mma_verify_gemm: the
 same emulation, compared bit for bit with a claimed D instead of stored)
 against a claimed D equal to the oracle's.  --splits S times the split-K
 schedule (mma_emulate_gemm_splitk: S runs of K/(16 S) steps, partial
-results added in FP32 round-to-nearest-even).
+results added in FP32 round-to-nearest-even).  --order reversed times the
+chain with its 256 K-steps in reversed order (mma_emulate_gemm_ordered).
 
 Prints ONE JSON line.  --gpus above 1 is refused: the library runs on one
 GPU (the path would shard over rows of D, with no exchange).
@@ -42,6 +43,15 @@ ALG_SLOTS_PER_MAC = {"ampere": 4.5 + 13 / 16, "hopper": 4.5 + 7 / 16}
 # MI355X integer VALU peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one
 # 32-bit lane operation per lane per clock.
 VALU_PEAK_OPS = 256 * 64 * 2.4e9
+# What roofline.achieved counts, stated in the line itself.
+UNIT_BASIS = ("algorithmic 32-bit VALU issue slots per emulated MAC (Ampere 5.3125, "
+              "Hopper 4.9375: product, alignment shift and signed add 1 each; exponent "
+              "add, running max and distance 1/2 each, two 16-bit exponents per 32-bit "
+              "lane; per output-step one normalisation per group and the FP32 range test) "
+              "x MACs / mean launch time, against 256 CU x 64 lanes x 2.4 GHz")
+# The oracle's worker threads: the CPUs this process may run on, at most 16
+# (one GPU's share of the host).
+CPU_THREADS_MAX = 16
 
 # name -> (model, model id, dtype name, dtype id, (input generator, seed),
 #          input description, the pages' CPU-simulator seconds for this
@@ -104,10 +114,16 @@ def parse():
                    help="time the audit compare against a claimed D instead of the GEMM")
     p.add_argument("--splits", type=int, default=1,
                    help="split-K schedule with this many runs (a divisor of K/16)")
+    p.add_argument("--order", choices=["forward", "reversed"], default="forward",
+                   help="K-step order of the chain (reversed: mma_emulate_gemm_ordered)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-seconds", type=float, default=10.0,
+    p.add_argument("--cpu-seconds", type=float, default=20.0,
                    help="target CPU work for the oracle sample")
-    p.add_argument("--cpu-threads", type=int, default=16)
+    p.add_argument("--cpu-threads", type=int, default=0,
+                   help="oracle threads (0: the CPUs this process may use, at most "
+                        f"{CPU_THREADS_MAX})")
+    p.add_argument("--cpu-full", action="store_true",
+                   help="time the oracle on the whole GEMM instead of a sample of rows")
     p.add_argument("--valu-peak", action="store_true",
                    help="instead of a workload, measure the issue rate of the hot loop's "
                         "VALU instructions (libvalurate.so) against the derived peak")
@@ -132,7 +148,8 @@ def bench_valu_peak(args):
 
     path = os.path.join(ROOT, "bit_exact_matrix_amd", "probe", "libvalurate.so")
     if not os.path.exists(path):
-        raise RuntimeError(f"{path} is missing: build it first (__graft_entry__.build())")
+        raise RuntimeError(f"{path} is missing: build it first "
+                           "(python -m bit_exact_matrix_amd.build probe)")
     import torch
     torch.cuda.init()
     lib = ctypes.CDLL(path)
@@ -253,6 +270,18 @@ def profile_record(name, kernel_hash):
     return rec
 
 
+def cpu_counts(requested):
+    """(threads the oracle uses, CPUs this process may run on, CPUs of the
+    host): the requested count, else the usable CPUs up to CPU_THREADS_MAX."""
+    host = os.cpu_count() or 1
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = host
+    threads = requested if requested > 0 else min(usable, CPU_THREADS_MAX)
+    return max(1, threads), usable, host
+
+
 def cpu_model():
     """The host CPU's model name (for the oracle baseline), if it can be read."""
     try:
@@ -331,7 +360,7 @@ def bench_tiles(args):
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
-        nth = max(1, min(args.cpu_threads, oracle.num_cpus()))
+        nth, usable, host = cpu_counts(args.cpu_threads)
         t = time.perf_counter()
         oracle.tiles(model, dtname, A[:1000], B[:1000], C[:1000], nthreads=nth)
         per = (time.perf_counter() - t) / 1000
@@ -340,6 +369,7 @@ def bench_tiles(args):
         Dr, Xr = oracle.tiles(model, dtname, A[:m], B[:m], C[:m], nthreads=nth)
         cs = time.perf_counter() - t
         cpu = {"value": round(m * 4096 / cs, 1), "unit": "MAC/s", "cores": nth,
+               "usable_cpus": usable, "host_cpus": host,
                "kind": "oracle", "cpu_model": cpu_model(), "seconds": round(cs, 2),
                "sample": f"tiles 0..{m - 1} of the batch",
                "sample_matches_gpu": bool(np.array_equal(Dr, D[:m]) and np.array_equal(Xr, X[:m]))}
@@ -356,7 +386,7 @@ def bench_tiles(args):
         "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3),
                      "peak": round(VALU_PEAK_OPS / 1e12, 3), "unit": "TOP/s",
                      "frac": round(achieved / VALU_PEAK_OPS, 4), "traffic": None,
-                     "alg_slots_per_mac": ALG_SLOTS_PER_MAC[model],
+                     "alg_slots_per_mac": ALG_SLOTS_PER_MAC[model], "unit_basis": UNIT_BASIS,
                      "launch_ms_mean": round(1e3 * avg_s, 4),
                      "launch_ms_min": launch_stats(launch_ms)[0],
                      "launch_ms_std": launch_stats(launch_ms)[1]},
@@ -377,8 +407,9 @@ def main():
     if args.shape:
         return bench_shape(args)
     if args.workload in TILE_WORKLOADS:
-        if args.verify or args.splits != 1:
-            print("--verify and --splits apply to the GEMM workloads", file=sys.stderr)
+        if args.verify or args.splits != 1 or args.order != "forward" or args.cpu_full:
+            print("--verify, --splits, --order and --cpu-full apply to the GEMM workloads",
+                  file=sys.stderr)
             sys.exit(2)
         bench_tiles(args)
         return
@@ -389,12 +420,14 @@ def main():
     import bit_exact_matrix_amd as mm
     from bit_exact_matrix_amd import inputs as I
 
-    if args.splits < 1 or (K // 16) % args.splits or (args.verify and args.splits != 1):
-        print("--splits must divide K/16 = 256 and cannot be combined with --verify",
-              file=sys.stderr)
+    if (args.splits < 1 or (K // 16) % args.splits
+            or sum((args.verify, args.splits != 1, args.order != "forward")) > 1):
+        print("--splits must divide K/16 = 256; --verify, --splits and --order are "
+              "exclusive", file=sys.stderr)
         sys.exit(2)
     model, model_id, dtname, dt_id, (gen, seed), data, pages_s = WORKLOADS[args.workload]
-    suffix = f"_splitk{args.splits}" if args.splits > 1 else ""
+    suffix = (f"_splitk{args.splits}" if args.splits > 1
+              else "_reversed" if args.order == "reversed" else "")
     mm.load_library()
     dev = torch.device("cuda:0")
     A, B, C = getattr(I, gen)(seed, M, N, K)
@@ -404,11 +437,18 @@ def main():
     tC = torch.from_numpy(C.view(np.float32)).to(dev)
     tD = torch.empty((M, N), dtype=torch.float32, device=dev)
     tX = torch.empty(M, dtype=torch.int32, device=dev)
+    tO = (torch.arange(K // 16 - 1, -1, -1, dtype=torch.int32, device=dev)
+          if args.order == "reversed" else None)
     stream = torch.cuda.current_stream()
 
     # one launch = the whole hot path (with the xorsum epilogue)
     def emulate():
-        if args.splits == 1:
+        if tO is not None:
+            rc = mm.mma_emulate_gemm_ordered_async(model_id, dt_id, tA.data_ptr(),
+                                                   tB.data_ptr(), tC.data_ptr(), tD.data_ptr(),
+                                                   M, N, K, tO.data_ptr(), tX.data_ptr(),
+                                                   stream.cuda_stream)
+        elif args.splits == 1:
             rc = mm.mma_emulate_gemm_async(model_id, dt_id, tA.data_ptr(), tB.data_ptr(),
                                            tC.data_ptr(), tD.data_ptr(), M, N, K,
                                            tX.data_ptr(), stream.cuda_stream)
@@ -507,7 +547,7 @@ def main():
                 "peak": round(VALU_PEAK_OPS / 1e12, 3), "unit": "TOP/s",
                 "frac": round(achieved / VALU_PEAK_OPS, 4),
                 "traffic": hbm["bytes_per_launch"] if hbm else None,
-                "alg_slots_per_mac": alg,
+                "alg_slots_per_mac": alg, "unit_basis": UNIT_BASIS,
                 "launch_ms_mean": round(1e3 * avg_launch_s, 4),
                 "launch_ms_min": launch_stats(launch_ms)[0],
                 "launch_ms_std": launch_stats(launch_ms)[1]}
@@ -522,34 +562,44 @@ def main():
     if not args.no_cpu_baseline:
         import oracle
         oracle.build(force=False)
-        nth = max(1, min(args.cpu_threads, oracle.num_cpus()))
-        # calibrate on a few rows, then time a sample worth ~cpu_seconds
+        nth, usable, host = cpu_counts(args.cpu_threads)
+
         def rows_of(n):
+            """Rows 0..n-1 of the same GEMM on the oracle."""
             if args.splits > 1:   # the split-K schedule on the first n rows
                 return oracle.gemm_splitk(model, dtname, A[:n], B, C[:n], args.splits,
                                           nthreads=nth)
+            if tO is not None:
+                return oracle.gemm_ordered(model, dtname, A, B, C, tO.cpu().numpy(),
+                                           nthreads=nth, rows=(0, n))
             return oracle.gemm_rows(model, dtname, A, B, C, 0, n, nthreads=nth)
-        t = time.perf_counter()
-        rows_of(nth)
-        per_row = (time.perf_counter() - t) / nth
-        rows = int(max(nth, min(M, args.cpu_seconds / max(per_row, 1e-9))))
-        rows = max(nth, (rows // nth) * nth)
+        if args.cpu_full:
+            rows = M
+        else:
+            # calibrate on a few rows, then time a sample worth ~cpu_seconds
+            t = time.perf_counter()
+            rows_of(nth)
+            per_row = (time.perf_counter() - t) / nth
+            rows = int(max(nth, min(M, args.cpu_seconds / max(per_row, 1e-9))))
+            rows = max(nth, (rows // nth) * nth)
         t = time.perf_counter()
         Dr, Xr = rows_of(rows)
         cs = time.perf_counter() - t
         cpu = {"value": round(rows * N * K / cs, 1), "unit": "MAC/s", "cores": nth,
+               "usable_cpus": usable, "host_cpus": host,
                "kind": "oracle", "cpu_model": cpu_model(), "seconds": round(cs, 2),
-               "sample": f"rows 0..{rows - 1} of D ({rows}x{N}x{K} MACs) of the same GEMM",
+               "sample": (f"the whole GEMM ({M}x{N}x{K} MACs)" if rows == M else
+                          f"rows 0..{rows - 1} of D ({rows}x{N}x{K} MACs) of the same GEMM"),
                "sample_matches_gpu": bool(np.array_equal(Dr, D[:rows])
                                           and (args.verify or np.array_equal(Xr, X[:rows])))}
-        if args.splits == 1:
+        if args.splits == 1 and tO is None:
             # one thread on a 256-column slice: the oracle's rate per core
             Bs = np.ascontiguousarray(B[:, :256])
             Cs = np.ascontiguousarray(C[:, :256])
             t = time.perf_counter()
             oracle.gemm_rows(model, dtname, A, Bs, Cs, 0, 4, nthreads=1)
             per_row = (time.perf_counter() - t) / 4
-            r1 = int(max(4, min(256, args.cpu_seconds / 3 / max(per_row, 1e-9))))
+            r1 = int(max(4, min(256, args.cpu_seconds / 6 / max(per_row, 1e-9))))
             t = time.perf_counter()
             Dp, _ = oracle.gemm_rows(model, dtname, A, Bs, Cs, 0, r1, nthreads=1)
             c1 = time.perf_counter() - t
@@ -563,6 +613,7 @@ def main():
         "metric": (f"bit-exact {'audit-compare' if args.verify else 'emulated'} MACs/s, "
                    f"4096³ {dtname.upper()} {model.capitalize()} model"
                    + (f", split-K {args.splits}" if args.splits > 1 else "")
+                   + (", K-steps reversed" if tO is not None else "")
                    + "; % of VALU peak"),
         "value": round(value, 1),
         "unit": "MAC/s",
@@ -572,7 +623,7 @@ def main():
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": round(value / (MACS / pages_s), 1),
+        "vs_baseline": None,
         "dtype": "int32",
         "data": data,
         "config": {"workload": args.workload + ("_verify" if args.verify else "") + suffix,
@@ -584,6 +635,11 @@ def main():
         "wall_s_timed": round(wall, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        # context only: the pages' CPU simulator on the same 4096x4096
+        # MatMul, another machine (Hawkeye notes, "Experiments and results",
+        # Table 1)
+        "context": {"pages_cpu_simulator_s": pages_s, "pages_hardware": "Apple M4 Pro",
+                    "ratio_to_pages_cpu_simulator": round(value / (MACS / pages_s), 1)},
     }
     print(json.dumps(out), flush=True)
 

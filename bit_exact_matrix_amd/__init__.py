@@ -6,13 +6,10 @@ ABI).  PyTorch supplies device memory and the current stream.  There is no
 CPU fallback: if the library is missing or no GPU is present, the calls
 raise.
 
-The raw C entry points are available under their own names
-(``mma_emulate_gemm``, ``mma_emulate_gemm_async``,
-``mma_emulate_gemm_splitk``, ``mma_emulate_gemm_splitk_async``,
-``mma_verify_gemm``, ``mma_verify_gemm_async``, ``mma_emulate_tiles``,
-``mma_emulate_strerror``, ``mma_emulate_spec_version``) and take integers
-(device pointers) exactly as the C functions do; ``gemm``, ``verify`` and
-``tiles`` wrap them for torch tensors.
+The raw C entry points are available under their own names (the
+``EXPORTED`` tuple) and take integers (device pointers) exactly as the C
+functions do; ``gemm``, ``verify`` and ``tiles`` wrap them for torch
+tensors.
 """
 from __future__ import annotations
 
@@ -27,8 +24,10 @@ FP16, BF16, FP8_E4M3 = 0, 1, 2
 MODELS = {"ampere": AMPERE, "hopper": HOPPER, "lovelace": LOVELACE}
 DTYPES = {"fp16": FP16, "bf16": BF16, "e4m3": FP8_E4M3, "fp8_e4m3": FP8_E4M3}
 EXPORTED = ("mma_emulate_gemm", "mma_emulate_gemm_async", "mma_emulate_gemm_splitk",
-            "mma_emulate_gemm_splitk_async", "mma_verify_gemm", "mma_verify_gemm_async",
-            "mma_emulate_tiles", "mma_emulate_strerror", "mma_emulate_spec_version")
+            "mma_emulate_gemm_splitk_async", "mma_emulate_gemm_ordered",
+            "mma_emulate_gemm_ordered_async", "mma_verify_gemm", "mma_verify_gemm_async",
+            "mma_emulate_tiles", "mma_emulate_workspace_held", "mma_emulate_strerror",
+            "mma_emulate_spec_version")
 
 
 class MmaEmuError(RuntimeError):
@@ -54,6 +53,11 @@ def load_library(path: str = LIB_PATH):
                                                 vp]
         lib.mma_emulate_gemm_splitk_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64,
                                                       i64, vp, vp]
+        lib.mma_emulate_gemm_ordered.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp,
+                                                 vp]
+        lib.mma_emulate_gemm_ordered_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64,
+                                                       vp, vp, vp]
+        lib.mma_emulate_workspace_held.argtypes = [i32, ctypes.POINTER(ctypes.c_uint64)]
         lib.mma_verify_gemm.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp]
         lib.mma_verify_gemm_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp, vp,
                                               vp]
@@ -63,9 +67,9 @@ def load_library(path: str = LIB_PATH):
         lib.mma_emulate_spec_version.argtypes = []
         for f in (lib.mma_emulate_gemm, lib.mma_emulate_gemm_async,
                   lib.mma_emulate_gemm_splitk, lib.mma_emulate_gemm_splitk_async,
-                  lib.mma_verify_gemm,
-                  lib.mma_verify_gemm_async, lib.mma_emulate_tiles,
-                  lib.mma_emulate_spec_version):
+                  lib.mma_emulate_gemm_ordered, lib.mma_emulate_gemm_ordered_async,
+                  lib.mma_verify_gemm, lib.mma_verify_gemm_async, lib.mma_emulate_tiles,
+                  lib.mma_emulate_workspace_held, lib.mma_emulate_spec_version):
             f.restype = i32
         _lib = lib
     return _lib
@@ -90,6 +94,25 @@ def mma_emulate_gemm_splitk_async(model, dtype, A, B, C, D, M, N, K, splits, xor
                                   hip_stream):
     return load_library().mma_emulate_gemm_splitk_async(model, dtype, A, B, C, D, M, N, K,
                                                         splits, xorsum_out, hip_stream)
+
+
+def mma_emulate_gemm_ordered(model, dtype, A, B, C, D, M, N, K, order, xorsum_out):
+    return load_library().mma_emulate_gemm_ordered(model, dtype, A, B, C, D, M, N, K, order,
+                                                   xorsum_out)
+
+
+def mma_emulate_gemm_ordered_async(model, dtype, A, B, C, D, M, N, K, order, xorsum_out,
+                                   hip_stream):
+    return load_library().mma_emulate_gemm_ordered_async(model, dtype, A, B, C, D, M, N, K,
+                                                         order, xorsum_out, hip_stream)
+
+
+def mma_emulate_workspace_held(device):
+    """(return code, bytes): the device memory the workspace pool of HIP
+    device `device` holds right now."""
+    v = ctypes.c_uint64(0)
+    rc = load_library().mma_emulate_workspace_held(int(device), ctypes.byref(v))
+    return rc, int(v.value)
 
 
 def mma_verify_gemm(model, dtype, A, B, C, D_claimed, M, N, K, report, row_diff_out):
@@ -173,12 +196,15 @@ def _matrix_shapes(A, B):
     return M, N, K
 
 
-def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None, splits=1):
+def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None, splits=1,
+         order=None):
     """Emulated D = C + A.B on the current stream.
 
     A: M x K and B: K x N device tensors of raw codes (2-byte elements for
     FP16/BF16, 1-byte for E4M3).  C: optional M x N float32 (bit patterns).
     splits > 1 selects the split-K schedule (mma_emulate_gemm_splitk).
+    order: optional int32 device tensor of K/16 entries, the K-step of each
+    chain position (mma_emulate_gemm_ordered); not with splits > 1.
     Returns (D, xorsum): D float32 M x N, xorsum int32 of M words (bit
     patterns of the per-row XOR) or None.
     """
@@ -189,16 +215,31 @@ def gemm(model, dtype, A, B, C=None, D=None, xorsum=False, stream=None, splits=1
     M, N, K = _matrix_shapes(A, B)
     _check_shape(C, (M, N), "C")
     _check_shape(D, (M, N), "D")
+    if order is not None:
+        if int(splits) != 1:
+            raise ValueError("a step order applies to the plain chain (splits = 1)")
+        _check_shape(order, (K // 16,), "order")
+        if order.dtype != torch.int32:
+            raise TypeError("order must be an int32 tensor")
     with torch.cuda.device(dev), torch.cuda.stream(s):
         if D is None:
             D = torch.empty((M, N), dtype=torch.float32, device=dev)
         X = torch.empty(M, dtype=torch.int32, device=dev) if xorsum else None
-        rc = mma_emulate_gemm_splitk_async(
-            m, d, _dev_ptr(A, "A", esz, dev), _dev_ptr(B, "B", esz, dev),
-            _dev_ptr(C, "C", 4, dev), _dev_ptr(D, "D", 4, dev), M, N, K, int(splits),
-            _dev_ptr(X, "xorsum", None, dev), s.cuda_stream)
+        if order is not None:
+            where = "mma_emulate_gemm_ordered_async"
+            rc = mma_emulate_gemm_ordered_async(
+                m, d, _dev_ptr(A, "A", esz, dev), _dev_ptr(B, "B", esz, dev),
+                _dev_ptr(C, "C", 4, dev), _dev_ptr(D, "D", 4, dev), M, N, K,
+                _dev_ptr(order, "order", 4, dev), _dev_ptr(X, "xorsum", None, dev),
+                s.cuda_stream)
+        else:
+            where = "mma_emulate_gemm_splitk_async"
+            rc = mma_emulate_gemm_splitk_async(
+                m, d, _dev_ptr(A, "A", esz, dev), _dev_ptr(B, "B", esz, dev),
+                _dev_ptr(C, "C", 4, dev), _dev_ptr(D, "D", 4, dev), M, N, K, int(splits),
+                _dev_ptr(X, "xorsum", None, dev), s.cuda_stream)
     if rc != 0:
-        raise MmaEmuError(rc, "mma_emulate_gemm_splitk_async")
+        raise MmaEmuError(rc, where)
     return D, X
 
 

@@ -1,4 +1,10 @@
-"""Build libmmaemu.so (and the VALU issue-rate probe) in-tree with hipcc for gfx950."""
+"""Build libmmaemu.so in-tree with hipcc for gfx950.
+
+``python -m bit_exact_matrix_amd.build`` builds the library;
+``python -m bit_exact_matrix_amd.build probe`` builds, in addition, the VALU
+issue-rate probe that ``bench.py --valu-peak`` loads (a measurement aid,
+not part of the library).
+"""
 from __future__ import annotations
 
 import os
@@ -45,11 +51,16 @@ def _hipcc(src: str, out: str, verbose: bool) -> str:
 
 
 def build(out: str = OUT, verbose: bool = False) -> str:
-    """libmmaemu.so (the library) and libvalurate.so (the VALU issue-rate
-    probe that bench.py --valu-peak runs)."""
-    _hipcc(PROBE_SRC, PROBE_OUT, verbose)
+    """libmmaemu.so, the library."""
     return _hipcc(os.path.join(CSRC, "mmaemu.hip"), out, verbose)
 
 
+def build_probe(verbose: bool = False) -> str:
+    """libvalurate.so, the VALU issue-rate probe of bench.py --valu-peak."""
+    return _hipcc(PROBE_SRC, PROBE_OUT, verbose)
+
+
 if __name__ == "__main__":
+    if len(sys.argv) > 1 and sys.argv[1] == "probe":
+        print(build_probe(verbose=True))
     print(build(verbose=True))

@@ -193,14 +193,15 @@ __device__ __forceinline__ uint32_t state_to_bits(int X, uint32_t ne) {
 
 // Recompute one output's step from the raw codes in global memory (rare
 // path): output (r, c) of the calling lane's 4x4 tile in the workgroup's
-// 64x64 block.  Rows and columns outside the matrix read the code of 1.0
+// 64x64 block, at chain position pos (the step order maps it to a K-step).  Rows and columns outside the matrix read the code of 1.0
 // (PAD_CODE), as in the image builders.  The row and column are derived
 // here rather than passed, so that the caller keeps no per-lane 64-bit
 // indices live across its loop.
 template <int MODEL, int DT>
 __device__ __noinline__ uint2 slow_step(const void* A, const void* B, int64_t M, int64_t N,
-                                        int64_t K, int64_t s, int tr, int tc, int Xold,
-                                        uint32_t ne_old) {
+                                        int64_t K, const int32_t* order, int64_t pos, int tr,
+                                        int tc, int Xold, uint32_t ne_old) {
+  const int64_t s = step_at(order, pos, K / 16);
   const int64_t row = (int64_t)blockIdx.y * BM + 4 * (threadIdx.x >> 4) + tr;
   const int64_t col = (int64_t)blockIdx.x * BN + 4 * (threadIdx.x & 15) + tc;
   uint32_t a[16], b[16];
@@ -327,15 +328,18 @@ __device__ __forceinline__ void poison_stage2(uint32_t (&ne)[16]) {
   if (sp) ne[8] = OP_SPECIAL;
 }
 
-// Pre-pass: build one operand's images of steps [t0, t0 + gridDim.x) (workspace
-// layout [block][step - t0][OpImage]), so the GEMM kernel only copies them
-// into LDS.  One 64-lane workgroup per (step, block); lane r owns row r of an
-// A block (IS_B false) or column r of a B block (IS_B true).
+// Pre-pass: build one operand's images of chain positions [t0, t0 + gridDim.x)
+// (workspace layout [block][position - t0][OpImage]), so the GEMM kernel only
+// copies them into LDS.  Position p holds K-step step_at(order, p): the
+// images are in chain order, whatever the step order.  One 64-lane workgroup
+// per (position, block); lane r owns row r of an A block (IS_B false) or
+// column r of a B block (IS_B true).
 template <int MODEL, int DT, bool IS_B>
 __global__ __launch_bounds__(64) void unpack_kernel(const void* __restrict__ src, int64_t limit,
                                                     int64_t K, int64_t N, int64_t t0,
+                                                    const int32_t* __restrict__ order,
                                                     uint32_t* __restrict__ ws) {
-  const int64_t s = t0 + blockIdx.x, blk = blockIdx.y;
+  const int64_t s = step_at(order, t0 + blockIdx.x, K / 16), blk = blockIdx.y;
   const int r = threadIdx.x;
   const int64_t idx = blk * 64 + r;
   OpImage* img = (OpImage*)(ws + (blk * gridDim.x + blockIdx.x) * IMG_WORDS);
@@ -693,7 +697,9 @@ constexpr int kWavesPerSimd = DMA ? 3 : 2;
 // With gridDim.z > 1 the z-th slice of the grid chains the ns steps that
 // start at s0 + z*ns instead, from +0 when z > 0, and stores into the D of
 // out moved on by z*zstride words: the runs of a split-K schedule side by
-// side.  The K loop is unrolled twice so that the accumulator state
+// side.  Steps are chain positions: position p applies K-step
+// step_at(order, p) (p itself when order is NULL); the workspace images are
+// already in position order.  The K loop is unrolled twice so that the accumulator state
 // alternates between two register sets instead of being copied back every
 // step.
 template <int MODEL, int DT, bool DMA>
@@ -701,7 +707,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C0, Sink out0,
     int64_t M, int64_t N, int64_t K, int64_t s00, int64_t ns,
     const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b, int64_t i0,
-    int64_t istride, int64_t zstride) {
+    int64_t istride, int64_t zstride, const int32_t* __restrict__ order) {
   __shared__ Stage stage[2];
   const int64_t z = blockIdx.z;
   const uint32_t* const C = z ? nullptr : C0;
@@ -741,7 +747,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
     if constexpr (DMA) {
       dma_step(&stage[s & 1], img_a + s * IMG_WORDS, img_b + s * IMG_WORDS, w, lane);
     } else {
-      fetch<DT>(A, B, M, N, K, bm, bn, s0 + s, t, ca, cb);
+      fetch<DT>(A, B, M, N, K, bm, bn, step_at(order, s0 + s, K / 16), t, ca, cb);
     }
   };
   auto end_fill = [&](int64_t s) {
@@ -760,7 +766,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
   // the exact recompute of output (r, c) of the lane's tile at step ks
   auto redo_at = [&](int64_t ks) {
     return [=](int r, int c, int x, uint32_t ne) {
-      return slow_step<MODEL, DT>(A, B, M, N, K, ks, r, c, x, ne);
+      return slow_step<MODEL, DT>(A, B, M, N, K, order, ks, r, c, x, ne);
     };
   };
   for (int64_t s = 0; s < nsteps; s += 2) {
@@ -870,6 +876,8 @@ inline int64_t gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return (mb + nb) * (K / 16) * (int64_t)sizeof(fastk::OpImage);
 }
 
+// order: NULL for the forward order, else the K-step of each chain position
+// (step_at); every schedule below works on chain positions.
 // ws: NULL for the in-kernel image build, else a workspace that holds the
 // images of ws_steps steps of every A block and every B block
 // (gemm_fast_workspace_bytes(M, N, 16 * ws_steps) bytes).
@@ -890,7 +898,8 @@ inline int64_t gemm_fast_workspace_bytes(int64_t M, int64_t N, int64_t K) {
 template <int MODEL, int DT>
 inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, const Sink& out,
                              int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_steps,
-                             hipStream_t s, int64_t splits = 1, uint32_t* partials = nullptr) {
+                             hipStream_t s, int64_t splits = 1, uint32_t* partials = nullptr,
+                             const int32_t* order = nullptr) {
   const int64_t mb = (M + fastk::BM - 1) / fastk::BM, nb = (N + fastk::BN - 1) / fastk::BN;
   const int64_t nsteps = K / 16, per = nsteps / splits;
   const dim3 grid((unsigned)nb, (unsigned)mb);
@@ -900,9 +909,9 @@ inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, co
   // the images of steps [t0, t0 + n), n <= ws_steps
   auto prepass = [&](int64_t t0, int64_t n) {
     fastk::unpack_kernel<MODEL, DT, false>
-        <<<dim3((unsigned)n, (unsigned)mb), dim3(64), 0, s>>>(A, M, K, N, t0, ws_a);
+        <<<dim3((unsigned)n, (unsigned)mb), dim3(64), 0, s>>>(A, M, K, N, t0, order, ws_a);
     fastk::unpack_kernel<MODEL, DT, true>
-        <<<dim3((unsigned)n, (unsigned)nb), dim3(64), 0, s>>>(B, N, K, N, t0, ws_b);
+        <<<dim3((unsigned)n, (unsigned)nb), dim3(64), 0, s>>>(B, N, K, N, t0, order, ws_b);
   };
   // steps [t0, t0 + n) from c into o, with the images of steps [i0, i0 + istride)
   // in the workspace (istride = 0: built in LDS)
@@ -910,10 +919,10 @@ inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, co
                    int64_t istride) {
     if (istride > 0) {
       fastk::gemm_fast_kernel<MODEL, DT, true><<<grid, dim3(fastk::NT), 0, s>>>(
-          A, B, c, o, M, N, K, t0, n, ws_a, ws_b, i0, istride, 0);
+          A, B, c, o, M, N, K, t0, n, ws_a, ws_b, i0, istride, 0, order);
     } else {
       fastk::gemm_fast_kernel<MODEL, DT, false><<<grid, dim3(fastk::NT), 0, s>>>(
-          A, B, c, o, M, N, K, t0, n, nullptr, nullptr, 0, 0, 0);
+          A, B, c, o, M, N, K, t0, n, nullptr, nullptr, 0, 0, 0, order);
     }
   };
   const bool whole = ws_steps >= nsteps;
@@ -927,7 +936,7 @@ inline void gemm_fast_launch(const void* A, const void* B, const uint32_t* C, co
     o.accumulate = 0;
     fastk::gemm_fast_kernel<MODEL, DT, true>
         <<<dim3((unsigned)nb, (unsigned)mb, (unsigned)splits), dim3(fastk::NT), 0, s>>>(
-            A, B, C, o, M, N, K, 0, per, ws_a, ws_b, 0, nsteps, M * N);
+            A, B, C, o, M, N, K, 0, per, ws_a, ws_b, 0, nsteps, M * N, order);
     const int64_t rows = M < 32768 ? M : 32768;
     fastk::reduce_runs_kernel<<<dim3((unsigned)((N + 255) / 256), (unsigned)rows), dim3(256),
                                 0, s>>>(partials, splits, M, N, out.D, out.xorsum);

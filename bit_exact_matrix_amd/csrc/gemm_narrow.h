@@ -112,14 +112,16 @@ __device__ __noinline__ uint2 redo_step(const void* A, const void* B, int64_t N,
   return make_uint2((uint32_t)X, ne);
 }
 
-// Chains the ns steps that start at step s0 for the 16x16 output tile
-// (blockIdx.y, blockIdx.x), from C (NULL: +0), into the sink.
-// Compiled for four waves per SIMD (128 VGPRs).
+// Chains the ns chain positions that start at s0 for the 16x16 output tile
+// (blockIdx.y, blockIdx.x), from C (NULL: +0), into the sink; position p
+// applies K-step step_at(order, p).  Compiled for four waves per SIMD (128
+// VGPRs).
 template <int MODEL, int DT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gemm_narrow_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
-    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns) {
+    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns, const int32_t* __restrict__ order) {
   constexpr int F = Model<MODEL>::F;
+  const int64_t T = K / 16;
   __shared__ NStage stage[2];
   const int tid = threadIdx.x, i = tid >> 4, j = tid & 15, wv = tid >> 6;
   const int64_t row = (int64_t)blockIdx.y * 16 + i, col = (int64_t)blockIdx.x * 16 + j;
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
   int X;
   uint32_t NE;
   bits_to_state<MODEL>((C && live) ? C[row * N + col] : 0u, X, NE);
-  if (ns > 0) load(s0);
+  if (ns > 0) load(step_at(order, s0, T));
   for (int64_t t = 0; t < ns; ++t) {
     NStage* st = &stage[t & 1];
     {
@@ -164,7 +166,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         st->bm[wv][j] = c4 << (4 * wv);
       }
     }
-    if (t + 1 < ns) load(s0 + t + 1);
+    if (t + 1 < ns) load(step_at(order, s0 + t + 1, T));
     __syncthreads();
 
     uint32_t av[16], ae[8], be[8];
@@ -214,7 +216,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
       NEn = NEn < NE_OVF ? NE_OVF : NEn;
     }
     if (bad && live) {
-      const uint2 r = redo_step<MODEL, DT>(A, B, N, K, s0 + t, row, col, X, NE);
+      const uint2 r =
+          redo_step<MODEL, DT>(A, B, N, K, step_at(order, s0 + t, T), row, col, X, NE);
       Xn = (int)r.x;
       NEn = r.y;
     }

@@ -24,11 +24,13 @@ constexpr int kSpecVersion = 1;
 // --------------------------------------------------- reference GEMM path
 // One lane per output, the chained steps read straight from global memory.
 // Kept as the simple, fully general path (any shape, any input bits).  It
-// chains the ns steps that start at step s0.
+// chains the ns chain positions that start at s0; position p applies K-step
+// step_at(order, p).
 template <int MODEL, int DT>
 __global__ __launch_bounds__(256) void gemm_reference_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
-    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns) {
+    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns,
+    const int32_t* __restrict__ order) {
   const int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const bool live = col < N;
   uint32_t nbad = 0;
@@ -37,7 +39,8 @@ __global__ __launch_bounds__(256) void gemm_reference_kernel(
     uint32_t c = 0, x = 0;
     if (live) {
       c = C ? C[row * N + col] : 0u;
-      for (int64_t t = s0; t < s0 + ns; ++t) {
+      for (int64_t p = s0; p < s0 + ns; ++p) {
+        const int64_t t = step_at(order, p, K / 16);
         uint32_t a[16], b[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
@@ -119,15 +122,16 @@ Range range_of(const void* p, int64_t bytes) {
   return Range{lo, p ? lo + (uintptr_t)bytes : lo};
 }
 
-// A, B, C read-only; D and xorsum written.  D == C exactly is allowed.
+// A, B, C and the step order O read-only; D and xorsum written.  D == C
+// exactly is allowed.
 int check_alias(const void* A, int64_t abytes, const void* B, int64_t bbytes,
                 const void* C, const void* D, int64_t cdbytes, const void* X,
-                int64_t xbytes) {
+                int64_t xbytes, const void* O = nullptr, int64_t obytes = 0) {
   const Range ra = range_of(A, abytes), rb = range_of(B, bbytes);
   const Range rc = range_of(C, cdbytes), rd = range_of(D, cdbytes);
-  const Range rx = range_of(X, xbytes);
+  const Range rx = range_of(X, xbytes), ro = range_of(O, obytes);
   if (overlap(rd, ra) || overlap(rd, rb) || overlap(rx, ra) || overlap(rx, rb) ||
-      overlap(rx, rc) || overlap(rx, rd))
+      overlap(rx, rc) || overlap(rx, rd) || overlap(rd, ro) || overlap(rx, ro))
     return MMAEMU_ERR_ALIAS;
   if (C && C != D && overlap(rc, rd)) return MMAEMU_ERR_ALIAS;
   return MMAEMU_OK;
@@ -145,6 +149,20 @@ int check_alias_verify(const void* A, int64_t abytes, const void* B, int64_t bby
   if (overlap(rr, rx)) return MMAEMU_ERR_ALIAS;
   for (const Range& r : in)
     if (overlap(rr, r) || overlap(rx, r)) return MMAEMU_ERR_ALIAS;
+  return MMAEMU_OK;
+}
+
+// Every pointer at the alignment of its elements: the kernels read and
+// write whole elements, and update the xorsum words (32-bit) and the
+// report (64-bit) with atomics, which need natural alignment.  NULL passes.
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_align(int dtype, const void* A, const void* B, const void* C, const void* D,
+                const void* X, const void* O = nullptr, const void* R = nullptr) {
+  const uintptr_t esz = dtype == MMAEMU_DTYPE_FP8_E4M3 ? 1 : 2;
+  if (!aligned(A, esz) || !aligned(B, esz) || !aligned(C, 4) || !aligned(D, 4) ||
+      !aligned(X, 4) || !aligned(O, 4) || !aligned(R, 8))
+    return MMAEMU_ERR_ALIGN;
   return MMAEMU_OK;
 }
 
@@ -207,20 +225,19 @@ int64_t narrow_blocks() {
 }
 
 // Stream-ordered workspace for the operand pre-pass, from one memory pool
-// per device.  The pool keeps up to the default cap of freed memory cached
-// (its release threshold), so repeated calls allocate no new device memory,
-// and returns the rest at the next synchronisation.  A failed allocation is
-// not an error: the caller falls back to the kernel that unpacks in place.
+// per device, created on first use.  Its release threshold is 0: memory that
+// a call frees (in stream order, after its kernels) goes back to the device
+// at the next synchronisation of the stream, an event or the device, and
+// the blocking entry points trim the pool after their own synchronisation,
+// so no workspace memory stays held between synchronised calls.  Freed
+// blocks are still reused by later calls enqueued before that
+// synchronisation.  A failed allocation is not an error: the caller falls
+// back to the kernel that builds its images in LDS.
 constexpr int kMaxDevices = 64;
 hipMemPool_t g_pool[kMaxDevices];
 std::once_flag g_pool_once[kMaxDevices];
 
-void* workspace_alloc(int64_t bytes, hipStream_t s) {
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
-    (void)hipGetLastError();
-    return nullptr;
-  }
+hipMemPool_t pool_of(int dev) {
   std::call_once(g_pool_once[dev], [dev] {
     hipMemPoolProps props;
     memset(&props, 0, sizeof props);
@@ -228,25 +245,67 @@ void* workspace_alloc(int64_t bytes, hipStream_t s) {
     props.location.type = hipMemLocationTypeDevice;
     props.location.id = dev;
     if (hipMemPoolCreate(&g_pool[dev], &props) == hipSuccess) {
-      uint64_t keep = (uint64_t)kDefaultWorkspaceCap;
+      uint64_t keep = 0;
       (void)hipMemPoolSetAttribute(g_pool[dev], hipMemPoolAttrReleaseThreshold, &keep);
     } else {
       g_pool[dev] = nullptr;
       (void)hipGetLastError();
     }
   });
-  if (!g_pool[dev]) return nullptr;
+  return g_pool[dev];
+}
+
+int current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  return dev;
+}
+
+void* workspace_alloc(int64_t bytes, hipStream_t s) {
+  const int dev = current_device();
+  if (dev < 0) return nullptr;
+  hipMemPool_t pool = pool_of(dev);
+  if (!pool) return nullptr;
   void* p = nullptr;
-  if (hipMallocFromPoolAsync(&p, (size_t)bytes, g_pool[dev], s) != hipSuccess) {
+  if (hipMallocFromPoolAsync(&p, (size_t)bytes, pool, s) != hipSuccess) {
     (void)hipGetLastError();
     return nullptr;
   }
   return p;
 }
 
+// After a blocking call's synchronisation: return what the pool of the
+// current device still holds (nothing of it is in use any more).
+void trim_workspace_pool() {
+  const int dev = current_device();
+  if (dev < 0) return;
+  hipMemPool_t pool = pool_of(dev);
+  if (pool && hipMemPoolTrimTo(pool, 0) != hipSuccess) (void)hipGetLastError();
+}
+
+// Where a GEMM's workspace comes from: the pool (fixed == NULL), or a buffer
+// of fixed_bytes that the caller of launch_gemm provides.
+struct WorkspaceSource {
+  void* fixed;
+  int64_t fixed_bytes;
+};
+
+// Everything launch_gemm needs besides the operands: the split-K run count,
+// the step order (NULL: forward) and the workspace source.
+struct Schedule {
+  int64_t splits;
+  const int32_t* order;
+  WorkspaceSource ws;
+};
+
 template <int MODEL, int DT>
 hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Sink& out,
-                       int64_t M, int64_t N, int64_t K, hipStream_t s, int64_t splits = 1) {
+                       int64_t M, int64_t N, int64_t K, hipStream_t s, const Schedule& sch) {
+  const int64_t splits = sch.splits;
+  const int32_t* const order = sch.order;
   // A plain chain taller than the tiled grids (65,535 blocks of 64 rows)
   // runs as row slices of that height: rows of D depend only on the same
   // rows of A and C, so a slice is the same GEMM on offset pointers.
@@ -260,7 +319,7 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
       if (out.xorsum) o.xorsum = out.xorsum + r0;
       const hipError_t e = launch_gemm<MODEL, DT>(
           (const char*)A + r0 * K * Fmt<DT>::bytes, B, C ? C + r0 * N : nullptr, o, m, N, K,
-          s);
+          s, sch);
       if (e != hipSuccess) return e;
     }
     return hipSuccess;
@@ -278,13 +337,18 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
       (nb_env >= 0 ? M * N / 4096 < nb_env : narrow_is_faster(M, N))) {
     narrowk::gemm_narrow_kernel<MODEL, DT>
         <<<dim3((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), dim3(256), 0, s>>>(
-            A, B, C, out, M, N, K, 0, K / 16);
+            A, B, C, out, M, N, K, 0, K / 16, order);
     return hipGetLastError();
   }
   if (gemm_fast_supported(M, N, K)) {
     const int64_t nsteps = K / 16, per = nsteps / splits;
     const int64_t step_bytes = gemm_fast_workspace_bytes(M, N, 16);
-    const int64_t cap = workspace_cap();
+    const bool fixed = sch.ws.fixed != nullptr;
+    const int64_t cap = fixed ? sch.ws.fixed_bytes : workspace_cap();
+    auto take = [&](int64_t bytes) -> void* {
+      if (fixed) return bytes <= sch.ws.fixed_bytes ? sch.ws.fixed : nullptr;
+      return workspace_alloc(bytes, s);
+    };
     void* ws = nullptr;
     int64_t ws_steps = 0;
     uint32_t* partials = nullptr;
@@ -293,7 +357,7 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
     const int64_t cd = M * N * 4;  // no overflow: checked with the shape
     if (splits > 1 && out.D && splits <= 65535 && cd <= cap / splits &&
         nsteps <= (cap - splits * cd) / step_bytes) {
-      ws = workspace_alloc(nsteps * step_bytes + splits * cd, s);
+      ws = take(nsteps * step_bytes + splits * cd);
       if (ws) {
         ws_steps = nsteps;
         partials = (uint32_t*)((char*)ws + nsteps * step_bytes);
@@ -305,10 +369,11 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
       ws_steps = cap / step_bytes;
       if (ws_steps > nsteps) ws_steps = nsteps;
       if (ws_steps < nsteps && ws_steps > per) ws_steps = per;
-      ws = ws_steps > 0 ? workspace_alloc(ws_steps * step_bytes, s) : nullptr;
+      ws = ws_steps > 0 ? take(ws_steps * step_bytes) : nullptr;
     }
-    gemm_fast_launch<MODEL, DT>(A, B, C, out, M, N, K, ws, ws_steps, s, splits, partials);
-    if (ws) {
+    gemm_fast_launch<MODEL, DT>(A, B, C, out, M, N, K, ws, ws_steps, s, splits, partials,
+                                order);
+    if (ws && !fixed) {
       // the free is ordered after the kernels; it is issued whatever the
       // launches returned, so that a failed call does not hold the memory
       const hipError_t e = hipGetLastError();
@@ -324,7 +389,7 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
       o.accumulate = r > 0;
       if (r + 1 < splits) o.xorsum = nullptr;
       gemm_reference_kernel<MODEL, DT><<<dim3((unsigned)cb, (unsigned)rows), dim3(256), 0, s>>>(
-          A, B, r == 0 ? C : nullptr, o, M, N, K, r * per, per);
+          A, B, r == 0 ? C : nullptr, o, M, N, K, r * per, per, order);
     }
   }
   return hipGetLastError();
@@ -371,26 +436,34 @@ int check_gemm_shape(int dtype, int64_t M, int64_t N, int64_t K, GemmBytes* g) {
 
 int gemm_impl(int model, int dtype, const void* A, const void* B, const float* C,
               float* D, int64_t M, int64_t N, int64_t K, uint32_t* xorsum,
-              hipStream_t s, int64_t splits = 1) {
+              hipStream_t s, const Schedule& sch, const char* where) {
   int rc = check_model_dtype(model, dtype);
   if (rc) return rc;
   GemmBytes g;
   rc = check_gemm_shape(dtype, M, N, K, &g);
   if (rc) return rc;
+  const int64_t splits = sch.splits;
   // split-K: a whole number of steps per run
   if (splits < 1 || (K == 0 ? splits != 1 : (K / 16) % splits != 0)) return MMAEMU_ERR_SHAPE;
   // an empty D: nothing to compute; the xorsum words of its M empty rows
   // are still written (as zeros)
   if (g.cd == 0 && !(xorsum && M > 0)) return MMAEMU_OK;
   if (g.cd > 0 && (!D || (K > 0 && (!A || !B)))) return MMAEMU_ERR_NULL;
+  // the step order is read only when there are steps and outputs
+  const int32_t* order = g.cd > 0 && K > 0 ? sch.order : nullptr;
+  rc = check_align(dtype, A, B, C, D, xorsum, order);
+  if (rc) return rc;
   rc = check_alias(g.cd && K ? A : nullptr, g.a, g.cd && K ? B : nullptr, g.b,
-                   g.cd ? C : nullptr, g.cd ? D : nullptr, g.cd, xorsum, xorsum ? M * 4 : 0);
+                   g.cd ? C : nullptr, g.cd ? D : nullptr, g.cd, xorsum, xorsum ? M * 4 : 0,
+                   order, order ? K / 16 * 4 : 0);
   if (rc) return rc;
   const Sink out{(uint32_t*)D, xorsum, nullptr, nullptr, 0};
+  Schedule run = sch;
+  run.order = order;
   clear_stale_hip_error();
   const hipError_t e = MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C,
-                                       out, M, N, K, s, splits);
-  if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm launch");
+                                       out, M, N, K, s, run);
+  if (e != hipSuccess) return hip_fail(e, where);
   return MMAEMU_OK;
 }
 
@@ -404,6 +477,8 @@ int verify_impl(int model, int dtype, const void* A, const void* B, const float*
   if (rc) return rc;
   if (!report) return MMAEMU_ERR_NULL;
   if (g.cd > 0 && (!D_claimed || (K > 0 && (!A || !B)))) return MMAEMU_ERR_NULL;
+  rc = check_align(dtype, A, B, C, D_claimed, row_diff, nullptr, report);
+  if (rc) return rc;
   const bool any = g.cd > 0;
   rc = check_alias_verify(any && K ? A : nullptr, g.a, any && K ? B : nullptr, g.b,
                           any ? C : nullptr, any ? D_claimed : nullptr, g.cd, report,
@@ -411,12 +486,24 @@ int verify_impl(int model, int dtype, const void* A, const void* B, const float*
   if (rc) return rc;
   const Sink out{nullptr, row_diff, (const uint32_t*)D_claimed, (unsigned long long*)report,
                  0};
+  const Schedule sch{1, nullptr, {nullptr, 0}};
   clear_stale_hip_error();
   const hipError_t e =
-      MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C, out, M, N, K, s);
+      MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C, out, M, N, K, s, sch);
   if (e != hipSuccess) return hip_fail(e, "mma_verify_gemm launch");
   return MMAEMU_OK;
 }
+
+// The end of a blocking call: synchronise the null stream, then hand the
+// workspace pool's memory back.
+int finish_blocking(const char* where) {
+  const hipError_t e = hipStreamSynchronize(nullptr);
+  if (e != hipSuccess) return hip_fail(e, where);
+  trim_workspace_pool();
+  return MMAEMU_OK;
+}
+
+const Schedule kPlain{1, nullptr, {nullptr, 0}};
 
 }  // namespace
 
@@ -425,33 +512,53 @@ extern "C" {
 int mma_emulate_gemm_async(int model, int dtype, const void* A, const void* B,
                            const float* C, float* D, int64_t M, int64_t N, int64_t K,
                            uint32_t* xorsum_out, void* hip_stream) {
-  return gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, (hipStream_t)hip_stream);
+  return gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, (hipStream_t)hip_stream,
+                   kPlain, "mma_emulate_gemm launch");
 }
 
 int mma_emulate_gemm(int model, int dtype, const void* A, const void* B, const float* C,
                      float* D, int64_t M, int64_t N, int64_t K, uint32_t* xorsum_out) {
-  const int rc = gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, nullptr);
+  const int rc = gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, nullptr, kPlain,
+                           "mma_emulate_gemm launch");
   if (rc) return rc;
-  const hipError_t e = hipStreamSynchronize(nullptr);
-  if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm synchronize");
-  return MMAEMU_OK;
+  return finish_blocking("mma_emulate_gemm synchronize");
 }
 
 int mma_emulate_gemm_splitk_async(int model, int dtype, const void* A, const void* B,
                                   const float* C, float* D, int64_t M, int64_t N, int64_t K,
                                   int64_t splits, uint32_t* xorsum_out, void* hip_stream) {
+  const Schedule sch{splits, nullptr, {nullptr, 0}};
   return gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, (hipStream_t)hip_stream,
-                   splits);
+                   sch, "mma_emulate_gemm_splitk launch");
 }
 
 int mma_emulate_gemm_splitk(int model, int dtype, const void* A, const void* B,
                             const float* C, float* D, int64_t M, int64_t N, int64_t K,
                             int64_t splits, uint32_t* xorsum_out) {
-  const int rc = gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, nullptr, splits);
+  const Schedule sch{splits, nullptr, {nullptr, 0}};
+  const int rc = gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, nullptr, sch,
+                           "mma_emulate_gemm_splitk launch");
   if (rc) return rc;
-  const hipError_t e = hipStreamSynchronize(nullptr);
-  if (e != hipSuccess) return hip_fail(e, "mma_emulate_gemm_splitk synchronize");
-  return MMAEMU_OK;
+  return finish_blocking("mma_emulate_gemm_splitk synchronize");
+}
+
+int mma_emulate_gemm_ordered_async(int model, int dtype, const void* A, const void* B,
+                                   const float* C, float* D, int64_t M, int64_t N, int64_t K,
+                                   const int32_t* order, uint32_t* xorsum_out,
+                                   void* hip_stream) {
+  const Schedule sch{1, order, {nullptr, 0}};
+  return gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, (hipStream_t)hip_stream,
+                   sch, "mma_emulate_gemm_ordered launch");
+}
+
+int mma_emulate_gemm_ordered(int model, int dtype, const void* A, const void* B,
+                             const float* C, float* D, int64_t M, int64_t N, int64_t K,
+                             const int32_t* order, uint32_t* xorsum_out) {
+  const Schedule sch{1, order, {nullptr, 0}};
+  const int rc = gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum_out, nullptr, sch,
+                           "mma_emulate_gemm_ordered launch");
+  if (rc) return rc;
+  return finish_blocking("mma_emulate_gemm_ordered synchronize");
 }
 
 int mma_verify_gemm_async(int model, int dtype, const void* A, const void* B,
@@ -468,9 +575,7 @@ int mma_verify_gemm(int model, int dtype, const void* A, const void* B, const fl
   const int rc =
       verify_impl(model, dtype, A, B, C, D_claimed, M, N, K, report, row_diff_out, nullptr);
   if (rc) return rc;
-  const hipError_t e = hipStreamSynchronize(nullptr);
-  if (e != hipSuccess) return hip_fail(e, "mma_verify_gemm synchronize");
-  return MMAEMU_OK;
+  return finish_blocking("mma_verify_gemm synchronize");
 }
 
 int mma_emulate_tiles(int model, int dtype, const void* A, const void* B, const float* C,
@@ -480,6 +585,8 @@ int mma_emulate_tiles(int model, int dtype, const void* A, const void* B, const 
   if (ntiles < 0 || ntiles > (int64_t)INT32_MAX) return MMAEMU_ERR_SHAPE;
   if (ntiles == 0) return MMAEMU_OK;
   if (!A || !B || !D) return MMAEMU_ERR_NULL;
+  rc = check_align(dtype, A, B, C, D, xorsum_out);
+  if (rc) return rc;
   const int64_t esz = dtype == MMAEMU_DTYPE_FP8_E4M3 ? 1 : 2;
   rc = check_alias(A, ntiles * 256 * esz, B, ntiles * 256 * esz, C, D, ntiles * 1024,
                    xorsum_out, xorsum_out ? ntiles * 4 : 0);
@@ -489,6 +596,25 @@ int mma_emulate_tiles(int model, int dtype, const void* A, const void* B, const 
       MMAEMU_DISPATCH(model, dtype, launch_tiles, A, B, (const uint32_t*)C, (uint32_t*)D,
                       xorsum_out, ntiles, (hipStream_t)hip_stream);
   if (e != hipSuccess) return hip_fail(e, "mma_emulate_tiles launch");
+  return MMAEMU_OK;
+}
+
+int mma_emulate_workspace_held(int device, uint64_t* bytes_out) {
+  if (!bytes_out) return MMAEMU_ERR_NULL;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess) {
+    const hipError_t e = hipGetLastError();
+    return hip_fail(e == hipSuccess ? hipErrorNoDevice : e, "mma_emulate_workspace_held");
+  }
+  if (device < 0 || device >= count || device >= kMaxDevices)
+    return hip_fail(hipErrorInvalidDevice, "mma_emulate_workspace_held");
+  *bytes_out = 0;
+  hipMemPool_t pool = pool_of(device);
+  if (!pool) return MMAEMU_OK;
+  uint64_t v = 0;
+  const hipError_t e = hipMemPoolGetAttribute(pool, hipMemPoolAttrReservedMemCurrent, &v);
+  if (e != hipSuccess) return hip_fail(e, "mma_emulate_workspace_held");
+  *bytes_out = v;
   return MMAEMU_OK;
 }
 
@@ -502,6 +628,9 @@ const char* mma_emulate_strerror(int code) {
     case MMAEMU_ERR_NULL: return "a required pointer is NULL";
     case MMAEMU_ERR_ALIAS: return "buffers overlap (only D == C is allowed)";
     case MMAEMU_ERR_HIP: return g_hip_error;
+    case MMAEMU_ERR_ALIGN:
+      return "a pointer is not aligned to its elements (codes 2 bytes for FP16/BF16; "
+             "C, D, xorsum and row words, step order 4 bytes; report 8 bytes)";
     default: return "unknown error code";
   }
 }

@@ -243,6 +243,15 @@ __device__ uint32_t step_generic(uint32_t c, const uint32_t (&a)[16],
   }
 }
 
+// The K-step that position pos of a chain applies: pos itself in the
+// forward order (order == NULL), else order[pos] read as an unsigned 32-bit
+// integer and clamped to the last of the T steps.
+__device__ __forceinline__ int64_t step_at(const int32_t* order, int64_t pos, int64_t T) {
+  if (!order) return pos;
+  const uint32_t v = (uint32_t)order[pos];
+  return (int64_t)v < T ? (int64_t)v : T - 1;
+}
+
 template <int DT>
 __device__ __forceinline__ uint32_t load_code(const void* p, int64_t idx) {
   if (Fmt<DT>::bytes == 1) return ((const uint8_t*)p)[idx];

@@ -35,31 +35,42 @@
  *
  * MEMORY AND LAYOUT
  *   Every pointer is a DEVICE pointer on the current HIP device, owned by
- *   the caller.  mma_emulate_gemm and mma_emulate_gemm_async stage the
- *   operands through a temporary workspace of operand images, 12 KiB per
- *   K-step for each 64-row block of A and each 64-column block of B: all
- *   K/16 steps take 12 KiB x (ceil(M/64) + ceil(N/64)) x K/16 bytes (384 MiB
- *   at 4096^3).  One call takes at most 1 GiB of it, or the byte count in
- *   the environment variable MMAEMU_WORKSPACE_MAX_BYTES (read on every
- *   call).  When the images of all steps do not fit, the call fills the
- *   workspace once per split-K run, or cuts the chain into runs of steps
- *   that restart from the D the previous one wrote (exact: every step's
- *   result is an FP32 value); the results are the same.  The workspace is
- *   allocated and freed in stream order from a per-device memory pool that
- *   the library creates on first use and keeps until the process ends,
- *   with up to 1 GiB of freed memory cached for later calls.  If the
- *   allocation fails, the cap is below one step's images, or the
- *   environment variable MMAEMU_NO_WORKSPACE is set, the call stages the
- *   operands in LDS instead (same results, slower) and allocates nothing.
- *   mma_emulate_tiles allocates nothing.  No other state is kept between
- *   calls.  A plain chain runs on a kernel with one lane per output, which
- *   needs no workspace, when an estimate of both kernels' time says it is
- *   the faster (small M * N, or a few rows against a wide N); setting the
- *   environment variable MMAEMU_NARROW_BLOCKS replaces that estimate by a
- *   threshold: that kernel below that many units of 4096 outputs (M * N),
- *   0 never; read on every call.  Shapes over 1,048,560 rows always run on
- *   the other kernels, and a plain GEMM over 4,194,240 rows runs in row
- *   slices of that height.  Either way the results are the same.
+ *   the caller, and aligned to its elements (codes: 2 bytes for FP16 and
+ *   BF16; C, D, fingerprint words and step orders: 4 bytes; the audit
+ *   report: 8 bytes).
+ *   WORKSPACE.  The GEMM entry points stage the operands through a
+ *   temporary workspace of operand images, 12 KiB per K-step for each
+ *   64-row block of A and each 64-column block of B: all K/16 steps take
+ *   12 KiB x (ceil(M/64) + ceil(N/64)) x K/16 bytes (384 MiB at 4096^3).
+ *   It is allocated and freed in stream order, around the call's kernels,
+ *   from a per-device memory pool that the library creates on first use.
+ *   The pool caches nothing: freed workspace returns to the device at the
+ *   next synchronisation of the stream, an event or the device, and a
+ *   blocking entry point hands it back before it returns, so between
+ *   synchronised calls the library holds no device memory
+ *   (mma_emulate_workspace_held reports what it holds).  One call takes at
+ *   most 1 GiB of workspace.  When the images of all steps do not fit, the
+ *   call fills the workspace once per split-K run, or cuts the chain into
+ *   runs of steps that restart from the D the previous one wrote (exact:
+ *   every step's result is an FP32 value); the results are the same.  If
+ *   the allocation fails, or one step's images exceed the cap, the call
+ *   stages the operands in LDS instead (same results, slower) and
+ *   allocates nothing.  mma_emulate_tiles allocates nothing.  No other
+ *   state is kept between calls.
+ *   KERNEL CHOICE.  A plain chain runs on a kernel with one lane per
+ *   output, which needs no workspace, when an estimate of both kernels'
+ *   time says it is the faster (small M * N, or a few rows against a wide
+ *   N).  Shapes over 1,048,560 rows always run on the other kernels, and a
+ *   plain GEMM over 4,194,240 rows runs in row slices of that height.
+ *   Whichever kernels run, the results are the same.
+ *   DIAGNOSTIC OVERRIDES.  Nothing needs to be set in the environment.
+ *   Three variables, read on every call and without effect when unset,
+ *   force the schedules above so that each can be tested on any shape:
+ *   MMAEMU_WORKSPACE_MAX_BYTES (a byte count) replaces the 1 GiB cap;
+ *   MMAEMU_NO_WORKSPACE (set to anything) stages every operand in LDS;
+ *   MMAEMU_NARROW_BLOCKS replaces the kernel estimate by a threshold: the
+ *   one-lane-per-output kernel below that many units of 4096 outputs
+ *   (M * N), 0 never.  None of them changes a result.
  *   A  M x K row-major raw codes: uint16 (FP16, BF16) or uint8 (E4M3)
  *   B  K x N row-major raw codes, same type
  *   C  M x N row-major FP32 (read as bit patterns); NULL means all +0.0
@@ -113,7 +124,8 @@ enum {
   MMAEMU_ERR_SHAPE = -4,       /* negative size, K not a multiple of 16, overflow */
   MMAEMU_ERR_NULL = -5,        /* a required pointer is NULL */
   MMAEMU_ERR_ALIAS = -6,       /* buffers overlap other than D == C */
-  MMAEMU_ERR_HIP = -7          /* a HIP launch or runtime call failed */
+  MMAEMU_ERR_HIP = -7,         /* a HIP launch or runtime call failed */
+  MMAEMU_ERR_ALIGN = -8        /* a pointer is not aligned to its elements */
 };
 
 /* Emulated GEMM, blocking: enqueued on the null stream of the current
@@ -160,6 +172,31 @@ int mma_emulate_gemm_splitk(int model, int dtype, const void *A, const void *B,
                             const float *C, float *D, int64_t M, int64_t N,
                             int64_t K, int64_t splits, uint32_t *xorsum_out);
 
+/* K-step order, an explicit model input.  The pages leave the order in
+ * which a production library walks K (its tile schedule) to later
+ * characterisation (Hawkeye notes, "Critical Analysis": the assumption
+ * stress test and the missing production path, Future work 4), and the
+ * rounding of every step makes the result depend on it.  This entry point
+ * chains the T = K/16 steps in a given order:
+ *   C_0 = C;  C_{p+1} = one MMA step of C_p with K-step t = order[p], i.e.
+ *   A[:, 16t .. 16t+15] and B[16t .. 16t+15, :];  D = C_T.
+ * order: NULL (the forward order 0, 1, .., T-1: mma_emulate_gemm_async), or
+ * a DEVICE array of T int32 entries, read-only, which may not overlap D or
+ * xorsum_out.  A permutation of 0..T-1 is the intended use; to give every
+ * input a defined result, an entry is read as an unsigned 32-bit integer
+ * and one at or past T takes step T-1.  Arguments, layouts, workspace,
+ * aliasing and errors otherwise as for mma_emulate_gemm_async.  Enqueued
+ * on hip_stream; returns after enqueue. */
+int mma_emulate_gemm_ordered_async(int model, int dtype, const void *A, const void *B,
+                                   const float *C, float *D, int64_t M, int64_t N,
+                                   int64_t K, const int32_t *order, uint32_t *xorsum_out,
+                                   void *hip_stream);
+
+/* Same contract, blocking (null stream, then synchronised). */
+int mma_emulate_gemm_ordered(int model, int dtype, const void *A, const void *B,
+                             const float *C, float *D, int64_t M, int64_t N, int64_t K,
+                             const int32_t *order, uint32_t *xorsum_out);
+
 /* Audit compare: the auditor's side of the Hawkeye workflow (Hawkeye notes,
  * "Problem and motivation" and "Relation to the verifiable-ML workflow": an
  * auditor who knows only which GPU architecture ran a MatMul recomputes it
@@ -202,6 +239,14 @@ int mma_verify_gemm(int model, int dtype, const void *A, const void *B,
 int mma_emulate_tiles(int model, int dtype, const void *A, const void *B,
                       const float *C, float *D, int64_t ntiles,
                       uint32_t *xorsum_out, void *hip_stream);
+
+/* Bytes of device memory that the workspace pool of HIP device `device`
+ * holds right now (0 before the pool exists), written to *bytes_out (host
+ * memory).  After a blocking entry point returns, and after any
+ * synchronisation that follows the asynchronous ones, it is 0.  Errors:
+ * MMAEMU_ERR_NULL for a NULL bytes_out, MMAEMU_ERR_HIP for a device that
+ * does not exist. */
+int mma_emulate_workspace_held(int device, uint64_t *bytes_out);
 
 /* Text for a return code (thread-local for MMAEMU_ERR_HIP: names the last
  * HIP error seen on this thread).  Never NULL. */

@@ -25,6 +25,7 @@ int main(void) {
   float *D = (float *)0x40000000;
   uint32_t *X = (uint32_t *)0x50000000;
   uint64_t *R = (uint64_t *)0x60000000;
+  const int32_t *O = (const int32_t *)0x70000000;
   EXPECT(mma_emulate_gemm(9, MMAEMU_DTYPE_FP16, A, B, C, D, 32, 32, 32, X), MMAEMU_ERR_MODEL);
   EXPECT(mma_emulate_gemm_async(MMAEMU_MODEL_AMPERE, 7, A, B, C, D, 32, 32, 32, X, NULL),
          MMAEMU_ERR_DTYPE);
@@ -40,6 +41,27 @@ int main(void) {
          MMAEMU_ERR_SHAPE);
   EXPECT(mma_emulate_tiles(MMAEMU_MODEL_HOPPER, MMAEMU_DTYPE_FP16, A, B, C, D, 0, X, NULL),
          MMAEMU_OK);
+  /* misaligned pointers: codes off their 2-byte elements, atomically
+     updated words off their natural alignment */
+  EXPECT(mma_emulate_gemm(MMAEMU_MODEL_AMPERE, MMAEMU_DTYPE_FP16, (const char *)A + 1, B, C,
+                          D, 32, 32, 32, X), MMAEMU_ERR_ALIGN);
+  EXPECT(mma_emulate_gemm_async(MMAEMU_MODEL_HOPPER, MMAEMU_DTYPE_BF16, A, B, C, D, 32, 32, 32,
+                                (uint32_t *)((char *)X + 2), NULL), MMAEMU_ERR_ALIGN);
+  EXPECT(mma_verify_gemm(MMAEMU_MODEL_HOPPER, MMAEMU_DTYPE_FP16, A, B, C, D, 32, 32, 32,
+                         (uint64_t *)((char *)R + 4), X), MMAEMU_ERR_ALIGN);
+  EXPECT(mma_emulate_tiles(MMAEMU_MODEL_AMPERE, MMAEMU_DTYPE_BF16, A, B, C,
+                           (float *)((char *)D + 2), 4, X, NULL), MMAEMU_ERR_ALIGN);
+  EXPECT(mma_emulate_gemm_ordered(MMAEMU_MODEL_AMPERE, MMAEMU_DTYPE_FP16, A, B, C, D, 32, 32,
+                                  32, (const int32_t *)((const char *)O + 2), X),
+         MMAEMU_ERR_ALIGN);
+  EXPECT(mma_emulate_gemm_ordered_async(MMAEMU_MODEL_HOPPER, MMAEMU_DTYPE_FP8_E4M3, A, B, C,
+                                        D, 32, 32, 32, (const int32_t *)D, X, NULL),
+         MMAEMU_ERR_ALIAS);
+  {
+    uint64_t held = 1;
+    EXPECT(mma_emulate_workspace_held(0, NULL), MMAEMU_ERR_NULL);
+    EXPECT(mma_emulate_workspace_held(-1, &held), MMAEMU_ERR_HIP);
+  }
   if (mma_emulate_spec_version() < 1) return 1;
   if (strcmp(mma_emulate_strerror(MMAEMU_OK), "ok") != 0) return 1;
   printf("c abi: ok\n");

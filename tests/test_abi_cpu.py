@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_strerror_and_version():
     assert mm.mma_emulate_spec_version() >= 1
-    for code in range(-7, 1):
+    for code in range(-8, 1):
         assert isinstance(mm.mma_emulate_strerror(code), str)
     assert "unknown" in mm.mma_emulate_strerror(42)
 
@@ -59,6 +59,52 @@ def test_gemm_argument_errors(args, code):
     assert mm.mma_emulate_gemm_async(*args, None) == code
 
 
+# misaligned pointers (an element's worth off): MMAEMU_ERR_ALIGN before any launch
+@pytest.mark.parametrize("args,code", [
+    ((0, 0, A + 1, B, C, D, 32, 32, 32, X), -8),        # FP16 codes at an odd address
+    ((1, 1, A, B + 1, C, D, 32, 32, 32, X), -8),        # BF16 codes at an odd address
+    ((0, 0, A, B, C + 2, D, 32, 32, 32, X), -8),        # C not 4-byte aligned
+    ((0, 0, A, B, C, D + 2, 32, 32, 32, X), -8),        # D not 4-byte aligned
+    ((0, 0, A, B, C, D, 32, 32, 32, X + 2), -8),        # xorsum not 4-byte aligned
+])
+def test_gemm_alignment_errors(args, code):
+    assert mm.mma_emulate_gemm_async(*args, None) == code
+    assert mm.mma_emulate_gemm_splitk_async(*args[:9], 1, args[9], None) == code
+    assert mm.mma_emulate_gemm_ordered_async(*args[:9], 0, args[9], None) == code
+
+
+O = 0x70000000  # fake step-order address
+
+
+@pytest.mark.parametrize("args,code", [
+    ((7, 0, A, B, C, D, 32, 32, 32, O, X), -1),          # unknown model
+    ((0, 2, A, B, C, D, 32, 32, 32, O, X), -3),          # E4M3 with Ampere
+    ((0, 0, A, B, C, D, 32, 32, 24, O, X), -4),          # K not a multiple of 16
+    ((0, 0, A, B, C, 0, 32, 32, 32, O, X), -5),          # NULL D
+    ((0, 0, A, B, C, D, 32, 32, 32, O + 2, X), -8),      # order not 4-byte aligned
+    ((0, 0, A, B, C, D, 32, 32, 32, D + 64, X), -6),     # order inside D (written)
+    ((0, 0, A, B, C, D, 32, 32, 32, X + 4, X), -6),      # order inside the xorsum words
+])
+def test_ordered_argument_errors(args, code):
+    assert mm.mma_emulate_gemm_ordered_async(*args, None) == code
+    assert mm.mma_emulate_gemm_ordered(*args) == code
+
+
+def test_ordered_order_may_overlap_the_inputs_and_is_unused_without_steps():
+    # the order is read-only, like A, B and C; with K = 0 (no steps) or an
+    # empty D it is never read, so its alignment does not matter either
+    assert mm.mma_emulate_gemm_ordered_async(0, 0, A, B, C, D, 0, 32, 32, A, X, None) == 0
+    assert mm.mma_emulate_gemm_ordered_async(0, 0, A, B, C, D, 0, 32, 32, O + 1, 0, None) == 0
+
+
+def test_workspace_held_arguments():
+    lib = mm.load_library()
+    assert lib.mma_emulate_workspace_held(0, None) == -5
+    rc, held = mm.mma_emulate_workspace_held(-1)
+    assert rc == -7 and held == 0          # no such device (or no GPU at all)
+    assert "mma_emulate_workspace_held" in mm.mma_emulate_strerror(-7)
+
+
 def test_gemm_empty_is_a_no_op():
     # an empty D with no xorsum words to write: nothing is enqueued (with
     # M > 0 rows and N = 0 the M xorsum words are written, on the GPU)
@@ -72,6 +118,8 @@ def test_gemm_empty_is_a_no_op():
     ((0, 0, A, B, C, D, -4, X), -4),
     ((0, 0, A, B, C, 0, 4, X), -5),
     ((0, 0, A, B, C, B, 4, X), -6),
+    ((0, 0, A + 1, B, C, D, 4, X), -8),
+    ((0, 0, A, B, C, D, 4, X + 2), -8),
 ])
 def test_tiles_argument_errors(args, code):
     assert mm.mma_emulate_tiles(*args, None) == code
@@ -100,6 +148,9 @@ R = 0x60000000  # fake report address
     ((0, 0, A, B, C, D, 32, 32, 32, R, A + 4), -6),    # row words inside A
     ((0, 0, A, B, C, D, 32, 32, 32, R, R + 8), -6),    # row words overlap the report
     ((0, 0, A, B, C, D, 32, 32, 32, C + 64, X), -6),   # report inside C
+    ((0, 0, A, B, C, D, 32, 32, 32, R + 4, X), -8),    # report not 8-byte aligned
+    ((0, 0, A, B, C, D + 1, 32, 32, 32, R, X), -8),    # claimed D not 4-byte aligned
+    ((0, 0, A, B, C, D, 32, 32, 32, R, X + 1), -8),    # row words not 4-byte aligned
 ])
 def test_verify_argument_errors(args, code):
     assert mm.mma_verify_gemm_async(*args, None) == code

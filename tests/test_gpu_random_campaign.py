@@ -5,8 +5,9 @@ Each case draws a model and format (Lovelace included), an input recipe
 normal inputs), a ragged shape (by default up to 299 x 299 x 640), and a
 path: the tiled kernel with its pre-pass, the tiled kernel building its
 images in LDS, the narrow kernel, the split-K schedule (a random divisor of
-the step count), the audit compare (0 to 4 planted bit flips), or a batch
-of up to 1999 independent tiles.  Every output word, fingerprint and
+the step count), a random K-step order (on one of the three chain kernels,
+now and then with repeated or out-of-range entries), the audit compare (0
+to 4 planted bit flips), or a batch of up to 1999 independent tiles.  Every output word, fingerprint and
 report must equal the oracle's.  MMAEMU_CAMPAIGN_CASES sets the number of cases (2000 by
 default; a run of 25,000 took about 4.5 minutes on one MI355X), and
 MMAEMU_CAMPAIGN_MAX_MN and MMAEMU_CAMPAIGN_MAX_STEPS the shape bounds (300
@@ -28,7 +29,7 @@ pytestmark = pytest.mark.gpu
 COMBOS = [("ampere", "fp16"), ("hopper", "fp16"), ("ampere", "bf16"), ("hopper", "bf16"),
           ("hopper", "e4m3"), ("lovelace", "fp16")]
 RECIPES = ["wide", "narrow", "coarse", "tiny", "specials", "normal"]
-PATHS = ["tiled", "tiled-in-lds", "narrow", "splitk", "verify", "tiles"]
+PATHS = ["tiled", "tiled-in-lds", "narrow", "splitk", "ordered", "verify", "tiles"]
 ENV = ("MMAEMU_NARROW_BLOCKS", "MMAEMU_NO_WORKSPACE")
 # shape bounds: M, N below MAX_MN, K up to 16 * MAX_STEPS
 MAX_MN = int(os.environ.get("MMAEMU_CAMPAIGN_MAX_MN", "300"))
@@ -95,6 +96,19 @@ def _one_case(torch_dev, orc, case):
         want = orc.compare(Dw, claimed)
         report, X = mm.verify(model, dt, *args, to_dev(torch_dev, claimed), row_diff=True)
         ok = mm.mismatches(report) == want[:2] and np.array_equal(to_host_bits(X), want[2])
+        return None if ok else what
+    if path == "ordered":
+        kernel = ("tiled", "tiled-in-lds", "narrow")[rng.integers(3)]
+        _set_path(kernel)
+        order = rng.permutation(T)
+        if rng.integers(4) == 0:
+            order = rng.integers(-2, T + 3, size=T)
+        order = order.astype(np.int32)
+        what += f" on {kernel}, order {order.tolist()}"
+        want, wx = orc.gemm_ordered(model, dt, A, B, C, order)
+        torch, dev = torch_dev
+        D, X = mm.gemm(model, dt, *args, xorsum=True, order=torch.from_numpy(order).to(dev))
+        ok = np.array_equal(to_host_bits(D), want) and np.array_equal(to_host_bits(X), wx)
         return None if ok else what
     splits = 1
     if path == "splitk":

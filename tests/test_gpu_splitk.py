@@ -5,8 +5,8 @@ import pytest
 
 import bit_exact_matrix_amd as mm
 from bit_exact_matrix_amd import inputs as I
-from test_gpu_parity import (COMBOS, FULL, _gen, assert_bits_equal, no_workspace,  # noqa: F401
-                             say, to_dev, to_host_bits, torch_dev)
+from test_gpu_parity import (COMBOS, DIGESTS, FULL, _gen, assert_bits_equal,  # noqa: F401
+                             no_workspace, say, sha, to_dev, to_host_bits, torch_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -53,9 +53,10 @@ def test_splitk_rejects_a_split_that_does_not_divide_the_steps(torch_dev):
             mm.gemm("ampere", "fp16", A, B, splits=bad)
 
 
-def test_splitk_full_size_sampled_rows(torch_dev, orc):
-    """4096^3 FP16 Ampere with 4 runs of 64 steps: sampled rows against the
-    oracle (rows are independent, so the oracle runs on those rows only)."""
+def test_splitk_full_size(torch_dev, orc):
+    """4096^3 FP16 Ampere with 4 runs of 64 steps: the whole output against
+    the oracle's stored digest, and sampled rows recomputed here (rows are
+    independent, so the oracle runs on those rows only)."""
     model, dt, gen = FULL["gemm_4096_fp16_ampere"]
     A, B, C = gen()
     say("split-K full size")
@@ -64,6 +65,9 @@ def test_splitk_full_size_sampled_rows(torch_dev, orc):
         want, wx = orc.gemm_splitk(model, dt, A[r0:r1], B, C[r0:r1], 4)
         assert_bits_equal(got[r0:r1], want, f"split-K full rows {r0}:{r1}")
         assert_bits_equal(gx[r0:r1], wx, f"split-K full xorsum rows {r0}:{r1}")
+    d = DIGESTS["gemm_4096_fp16_ampere_splitk4"]
+    assert sha(got) == d["D_sha256"], "split-K 4096^3: D differs from the oracle's"
+    assert sha(gx) == d["xorsum_sha256"], "split-K 4096^3: xorsum differs from the oracle's"
 
 
 @pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("hopper", "bf16"),
