@@ -24,7 +24,8 @@ FP16, BF16, FP8_E4M3 = 0, 1, 2
 MODELS = {"ampere": AMPERE, "hopper": HOPPER, "lovelace": LOVELACE}
 DTYPES = {"fp16": FP16, "bf16": BF16, "e4m3": FP8_E4M3, "fp8_e4m3": FP8_E4M3}
 EXPORTED = ("mma_emulate_gemm", "mma_emulate_gemm_async", "mma_emulate_gemm_splitk",
-            "mma_emulate_gemm_splitk_async", "mma_emulate_gemm_ordered",
+            "mma_emulate_gemm_splitk_async", "mma_emulate_gemm_noalloc_async",
+            "mma_emulate_gemm_ordered",
             "mma_emulate_gemm_ordered_async", "mma_verify_gemm", "mma_verify_gemm_async",
             "mma_emulate_tiles", "mma_emulate_workspace_held", "mma_emulate_strerror",
             "mma_emulate_spec_version")
@@ -53,6 +54,8 @@ def load_library(path: str = LIB_PATH):
                                                 vp]
         lib.mma_emulate_gemm_splitk_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64,
                                                       i64, vp, vp]
+        lib.mma_emulate_gemm_noalloc_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64,
+                                                       vp, vp]
         lib.mma_emulate_gemm_ordered.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64, vp,
                                                  vp]
         lib.mma_emulate_gemm_ordered_async.argtypes = [i32, i32, vp, vp, vp, vp, i64, i64, i64,
@@ -67,6 +70,7 @@ def load_library(path: str = LIB_PATH):
         lib.mma_emulate_spec_version.argtypes = []
         for f in (lib.mma_emulate_gemm, lib.mma_emulate_gemm_async,
                   lib.mma_emulate_gemm_splitk, lib.mma_emulate_gemm_splitk_async,
+                  lib.mma_emulate_gemm_noalloc_async,
                   lib.mma_emulate_gemm_ordered, lib.mma_emulate_gemm_ordered_async,
                   lib.mma_verify_gemm, lib.mma_verify_gemm_async, lib.mma_emulate_tiles,
                   lib.mma_emulate_workspace_held, lib.mma_emulate_spec_version):
@@ -94,6 +98,11 @@ def mma_emulate_gemm_splitk_async(model, dtype, A, B, C, D, M, N, K, splits, xor
                                   hip_stream):
     return load_library().mma_emulate_gemm_splitk_async(model, dtype, A, B, C, D, M, N, K,
                                                         splits, xorsum_out, hip_stream)
+
+
+def mma_emulate_gemm_noalloc_async(model, dtype, A, B, C, D, M, N, K, xorsum_out, hip_stream):
+    return load_library().mma_emulate_gemm_noalloc_async(model, dtype, A, B, C, D, M, N, K,
+                                                         xorsum_out, hip_stream)
 
 
 def mma_emulate_gemm_ordered(model, dtype, A, B, C, D, M, N, K, order, xorsum_out):

@@ -286,6 +286,35 @@ void trim_workspace_pool() {
   if (pool && hipMemPoolTrimTo(pool, 0) != hipSuccess) (void)hipGetLastError();
 }
 
+// The workspace of mma_emulate_gemm_noalloc_async: a fixed array of device
+// memory, one copy per GPU the library runs on, held until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is taken once per device with hipGetSymbolAddress (while
+// that device is current) and only that address is ever handed to a kernel.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// The device address of the current device's scratch array (NULL and the
+// HIP error if it cannot be taken).
+void* scratch_of(int dev, hipError_t* err) {
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      p = nullptr;
+    }
+    g_scratch[dev] = p;
+    g_scratch_err[dev] = e;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch[dev];
+}
+
 // Where a GEMM's workspace comes from: the pool (fixed == NULL), or a buffer
 // of fixed_bytes that the caller of launch_gemm provides.
 struct WorkspaceSource {
@@ -301,17 +330,40 @@ struct Schedule {
   WorkspaceSource ws;
 };
 
+// A plain chain taller than the tiled grids (65,535 blocks of 64 rows)
+// runs as row slices of that height: rows of D depend only on the same
+// rows of A and C, so a slice is the same GEMM on offset pointers.
+constexpr int64_t kSliceRows = int64_t(65535) * fastk::BM;
+
+bool row_slices(int64_t M, int64_t N, int64_t K, int64_t splits, const Sink& out) {
+  return M > kSliceRows && splits == 1 && !out.claimed && !out.accumulate &&
+         gemm_fast_supported(kSliceRows, N, K);
+}
+
+// The narrow kernel takes a plain chain that it is estimated to run faster
+// (or that MMAEMU_NARROW_BLOCKS sends to it); its grid's y dimension, 16
+// rows a block, stays within 65,535 blocks, as the tiled grid's does.
+bool takes_narrow(int64_t M, int64_t N, int64_t K, int64_t splits) {
+  if (!gemm_fast_supported(M, N, K) || splits != 1 || (M + 15) / 16 > 65535) return false;
+  const int64_t nb_env = narrow_blocks();
+  return nb_env >= 0 ? M * N / 4096 < nb_env : narrow_is_faster(M, N);
+}
+
+// The workspace one K-step of a plain chain needs on the kernel the
+// library picks for it: the operand images of the tiled kernel, else 0.
+int64_t chain_step_bytes(int64_t M, int64_t N, int64_t K, const Sink& out) {
+  if (M == 0 || N == 0) return 0;
+  if (row_slices(M, N, K, 1, out)) return gemm_fast_workspace_bytes(kSliceRows, N, 16);
+  if (takes_narrow(M, N, K, 1) || !gemm_fast_supported(M, N, K)) return 0;
+  return gemm_fast_workspace_bytes(M, N, 16);
+}
+
 template <int MODEL, int DT>
 hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Sink& out,
                        int64_t M, int64_t N, int64_t K, hipStream_t s, const Schedule& sch) {
   const int64_t splits = sch.splits;
   const int32_t* const order = sch.order;
-  // A plain chain taller than the tiled grids (65,535 blocks of 64 rows)
-  // runs as row slices of that height: rows of D depend only on the same
-  // rows of A and C, so a slice is the same GEMM on offset pointers.
-  constexpr int64_t kSliceRows = int64_t(65535) * fastk::BM;
-  if (M > kSliceRows && splits == 1 && !out.claimed && !out.accumulate &&
-      gemm_fast_supported(kSliceRows, N, K)) {
+  if (row_slices(M, N, K, splits, out)) {
     for (int64_t r0 = 0; r0 < M; r0 += kSliceRows) {
       const int64_t m = M - r0 < kSliceRows ? M - r0 : kSliceRows;
       Sink o = out;
@@ -330,11 +382,7 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
   }
   if (out.report) init_report_kernel<<<dim3(1), dim3(64), 0, s>>>(out.report);
   if (M == 0 || N == 0) return hipGetLastError();
-  // (the narrow grid's y dimension, 16 rows a block, stays within 65,535
-  // blocks, as the tiled grid's does; a taller shape runs tiled)
-  const int64_t nb_env = narrow_blocks();
-  if (gemm_fast_supported(M, N, K) && splits == 1 && (M + 15) / 16 <= 65535 &&
-      (nb_env >= 0 ? M * N / 4096 < nb_env : narrow_is_faster(M, N))) {
+  if (takes_narrow(M, N, K, splits)) {
     narrowk::gemm_narrow_kernel<MODEL, DT>
         <<<dim3((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), dim3(256), 0, s>>>(
             A, B, C, out, M, N, K, 0, K / 16, order);
@@ -434,9 +482,12 @@ int check_gemm_shape(int dtype, int64_t M, int64_t N, int64_t K, GemmBytes* g) {
   return MMAEMU_OK;
 }
 
-int gemm_impl(int model, int dtype, const void* A, const void* B, const float* C,
-              float* D, int64_t M, int64_t N, int64_t K, uint32_t* xorsum,
-              hipStream_t s, const Schedule& sch, const char* where) {
+// Every argument check of a GEMM call, before anything touches the device.
+// Sets *nothing when the call has nothing to do.
+int gemm_check(int model, int dtype, const void* A, const void* B, const float* C, float* D,
+               int64_t M, int64_t N, int64_t K, uint32_t* xorsum, const Schedule& sch,
+               bool* nothing) {
+  *nothing = false;
   int rc = check_model_dtype(model, dtype);
   if (rc) return rc;
   GemmBytes g;
@@ -447,19 +498,29 @@ int gemm_impl(int model, int dtype, const void* A, const void* B, const float* C
   if (splits < 1 || (K == 0 ? splits != 1 : (K / 16) % splits != 0)) return MMAEMU_ERR_SHAPE;
   // an empty D: nothing to compute; the xorsum words of its M empty rows
   // are still written (as zeros)
-  if (g.cd == 0 && !(xorsum && M > 0)) return MMAEMU_OK;
+  if (g.cd == 0 && !(xorsum && M > 0)) {
+    *nothing = true;
+    return MMAEMU_OK;
+  }
   if (g.cd > 0 && (!D || (K > 0 && (!A || !B)))) return MMAEMU_ERR_NULL;
   // the step order is read only when there are steps and outputs
   const int32_t* order = g.cd > 0 && K > 0 ? sch.order : nullptr;
   rc = check_align(dtype, A, B, C, D, xorsum, order);
   if (rc) return rc;
-  rc = check_alias(g.cd && K ? A : nullptr, g.a, g.cd && K ? B : nullptr, g.b,
-                   g.cd ? C : nullptr, g.cd ? D : nullptr, g.cd, xorsum, xorsum ? M * 4 : 0,
-                   order, order ? K / 16 * 4 : 0);
-  if (rc) return rc;
+  return check_alias(g.cd && K ? A : nullptr, g.a, g.cd && K ? B : nullptr, g.b,
+                     g.cd ? C : nullptr, g.cd ? D : nullptr, g.cd, xorsum, xorsum ? M * 4 : 0,
+                     order, order ? K / 16 * 4 : 0);
+}
+
+int gemm_impl(int model, int dtype, const void* A, const void* B, const float* C,
+              float* D, int64_t M, int64_t N, int64_t K, uint32_t* xorsum,
+              hipStream_t s, const Schedule& sch, const char* where) {
+  bool nothing = false;
+  const int rc = gemm_check(model, dtype, A, B, C, D, M, N, K, xorsum, sch, &nothing);
+  if (rc || nothing) return rc;
   const Sink out{(uint32_t*)D, xorsum, nullptr, nullptr, 0};
   Schedule run = sch;
-  run.order = order;
+  if (M * N == 0 || K == 0) run.order = nullptr;
   clear_stale_hip_error();
   const hipError_t e = MMAEMU_DISPATCH(model, dtype, launch_gemm, A, B, (const uint32_t*)C,
                                        out, M, N, K, s, run);
@@ -505,6 +566,26 @@ int finish_blocking(const char* where) {
 
 const Schedule kPlain{1, nullptr, {nullptr, 0}};
 
+// mma_emulate_gemm_async on the static scratch array instead of the pool.
+int gemm_noalloc(int model, int dtype, const void* A, const void* B, const float* C, float* D,
+                 int64_t M, int64_t N, int64_t K, uint32_t* xorsum, hipStream_t s) {
+  bool nothing = false;
+  const int rc = gemm_check(model, dtype, A, B, C, D, M, N, K, xorsum, kPlain, &nothing);
+  if (rc || nothing) return rc;
+  // the same decision the launch makes: reject a shape whose chain needs
+  // more than the scratch for even one K-step of operand images
+  const Sink probe{(uint32_t*)D, xorsum, nullptr, nullptr, 0};
+  if (K > 0 && chain_step_bytes(M, N, K, probe) > kScratchBytes) return MMAEMU_ERR_SCRATCH;
+  const int dev = current_device();
+  if (dev < 0) return hip_fail(hipErrorNoDevice, "mma_emulate_gemm_noalloc_async");
+  hipError_t e = hipSuccess;
+  void* ws = scratch_of(dev, &e);
+  if (!ws) return hip_fail(e, "mma_emulate_gemm_noalloc_async: scratch address");
+  const Schedule sch{1, nullptr, {ws, kScratchBytes}};
+  return gemm_impl(model, dtype, A, B, C, D, M, N, K, xorsum, s, sch,
+                   "mma_emulate_gemm_noalloc_async launch");
+}
+
 }  // namespace
 
 extern "C" {
@@ -522,6 +603,12 @@ int mma_emulate_gemm(int model, int dtype, const void* A, const void* B, const f
                            "mma_emulate_gemm launch");
   if (rc) return rc;
   return finish_blocking("mma_emulate_gemm synchronize");
+}
+
+int mma_emulate_gemm_noalloc_async(int model, int dtype, const void* A, const void* B,
+                                   const float* C, float* D, int64_t M, int64_t N, int64_t K,
+                                   uint32_t* xorsum_out, void* hip_stream) {
+  return gemm_noalloc(model, dtype, A, B, C, D, M, N, K, xorsum_out, (hipStream_t)hip_stream);
 }
 
 int mma_emulate_gemm_splitk_async(int model, int dtype, const void* A, const void* B,
@@ -628,6 +715,9 @@ const char* mma_emulate_strerror(int code) {
     case MMAEMU_ERR_NULL: return "a required pointer is NULL";
     case MMAEMU_ERR_ALIAS: return "buffers overlap (only D == C is allowed)";
     case MMAEMU_ERR_HIP: return g_hip_error;
+    case MMAEMU_ERR_SCRATCH:
+      return "the chain needs more than the 64 MiB static scratch for one K-step of "
+             "operand images (ceil(M/64) + ceil(N/64) > 5461)";
     case MMAEMU_ERR_ALIGN:
       return "a pointer is not aligned to its elements (codes 2 bytes for FP16/BF16; "
              "C, D, xorsum and row words, step order 4 bytes; report 8 bytes)";

@@ -125,7 +125,8 @@ enum {
   MMAEMU_ERR_NULL = -5,        /* a required pointer is NULL */
   MMAEMU_ERR_ALIAS = -6,       /* buffers overlap other than D == C */
   MMAEMU_ERR_HIP = -7,         /* a HIP launch or runtime call failed */
-  MMAEMU_ERR_ALIGN = -8        /* a pointer is not aligned to its elements */
+  MMAEMU_ERR_ALIGN = -8,       /* a pointer is not aligned to its elements */
+  MMAEMU_ERR_SCRATCH = -9      /* mma_emulate_gemm_noalloc_async: beyond its scratch */
 };
 
 /* Emulated GEMM, blocking: enqueued on the null stream of the current
@@ -140,6 +141,26 @@ int mma_emulate_gemm(int model, int dtype, const void *A, const void *B,
 int mma_emulate_gemm_async(int model, int dtype, const void *A, const void *B,
                            const float *C, float *D, int64_t M, int64_t N,
                            int64_t K, uint32_t *xorsum_out, void *hip_stream);
+
+/* Allocation-free variant of mma_emulate_gemm_async, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Same arguments, results and
+ * errors as mma_emulate_gemm_async; it calls no allocator.  Its workspace is
+ * a static array of 64 MiB of device memory that the library holds on every
+ * GPU it runs on until the process ends, shared by every call on that GPU:
+ * calls that overlap on one GPU (on two streams, or from two threads without
+ * ordering between them) race on it, so the caller must order them.  Nothing
+ * in it needs clearing: each call writes every operand image it reads, and
+ * the fingerprint words are cleared on the stream by a kernel.  A chain whose
+ * operand images for one K-step exceed the 64 MiB (the tiled kernel with
+ * ceil(M/64) + ceil(N/64) > 5461) is rejected with MMAEMU_ERR_SCRATCH before
+ * anything is enqueued; a longer chain runs in chunks of as many K-steps as
+ * fit, each restarting from the D the previous chunk wrote (the same
+ * results).  The workspace overrides of the environment do not apply to
+ * it. */
+int mma_emulate_gemm_noalloc_async(int model, int dtype, const void *A, const void *B,
+                                   const float *C, float *D, int64_t M, int64_t N,
+                                   int64_t K, uint32_t *xorsum_out, void *hip_stream);
 
 /* Split-K schedule, an explicit model input.  The pages name split-K (and
  * atomic accumulation) as ways a production library may compose tiles

@@ -30,7 +30,7 @@ def test_library_loads_and_exports_every_declared_symbol():
 
 def test_strerror_and_version():
     assert mm.mma_emulate_spec_version() >= 1
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert isinstance(mm.mma_emulate_strerror(code), str)
     assert "unknown" in mm.mma_emulate_strerror(42)
 
@@ -95,6 +95,24 @@ def test_ordered_order_may_overlap_the_inputs_and_is_unused_without_steps():
     # empty D it is never read, so its alignment does not matter either
     assert mm.mma_emulate_gemm_ordered_async(0, 0, A, B, C, D, 0, 32, 32, A, X, None) == 0
     assert mm.mma_emulate_gemm_ordered_async(0, 0, A, B, C, D, 0, 32, 32, O + 1, 0, None) == 0
+
+
+def test_noalloc_argument_errors():
+    """The allocation-free GEMM validates like mma_emulate_gemm_async, and
+    rejects a chain whose one K-step of operand images exceeds its 64 MiB
+    scratch (ceil(M/64) + ceil(N/64) > 5461 on the tiled kernel) with
+    MMAEMU_ERR_SCRATCH, all before any HIP call."""
+    f = mm.mma_emulate_gemm_noalloc_async
+    assert f(7, 0, A, B, C, D, 32, 32, 32, X, None) == -1
+    assert f(0, 2, A, B, C, D, 32, 32, 32, X, None) == -3
+    assert f(0, 0, A, B, C, D, 32, 32, 24, X, None) == -4
+    assert f(0, 0, A + 1, B, C, D, 32, 32, 32, X, None) == -8
+    assert f(0, 0, A, B, C, A + 64, 32, 32, 32, X, None) == -6
+    big = (1 << 40, 2 << 40, 3 << 40, 4 << 40)   # 1 TiB apart: no overlap
+    assert f(0, 0, *big, 200000, 200000, 64, None, None) == -9
+    assert f(1, 1, *big, 349441, 64, 16, None, None) == -9      # 5461 + 1 blocks of 64
+    assert f(0, 0, 0, 0, 0, 0, 0, 200000, 64, 0, None) == 0      # nothing to compute
+    assert "scratch" in mm.mma_emulate_strerror(-9)
 
 
 def test_workspace_held_arguments():
