@@ -308,6 +308,19 @@ def kernel_source_hash():
     return h.hexdigest()
 
 
+def copy_calibration(dev):
+    """A plain 256 MiB device copy, twice: the reference whose known bytes
+    scale the HBM byte counters (FETCH_SIZE, WRITE_SIZE) of a profiled run."""
+    import torch
+    src = torch.empty(64 << 20, dtype=torch.int32, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def bench_tiles(args):
     """Time one mma_emulate_tiles call per step on a batch of independent
     16x16x16 steps (the pages' random-tile check); parity by the oracle's
@@ -350,12 +363,17 @@ def bench_tiles(args):
     wall = time.perf_counter() - t0
     launch_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
     avg_s = sum(launch_ms) / 1e3 / args.steps
+    if args.copy_calibration:
+        copy_calibration(dev)
     D = tD.cpu().numpy().view(np.uint32)
     X = tX.cpu().numpy().view(np.uint32)
     ref = json.load(open(os.path.join(ROOT, "tests", "golden", "oracle_digests.json")))[dkey]
     bit_exact = (hashlib.sha256(D.tobytes()).hexdigest() == ref["D_sha256"]
                  and hashlib.sha256(X.tobytes()).hexdigest() == ref["xorsum_sha256"])
     achieved = ALG_SLOTS_PER_MAC[model] * macs / avg_s
+    khash = kernel_source_hash()
+    hbm = profile_record(args.workload + "_hbm_traffic.json", khash)
+    valu = profile_record(args.workload + "_valu_counters.json", khash)
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -385,13 +403,18 @@ def bench_tiles(args):
         "bit_exact_vs_oracle": bool(bit_exact), "wall_s_timed": round(wall, 4),
         "roofline": {"bound": "alu", "achieved": round(achieved / 1e12, 3),
                      "peak": round(VALU_PEAK_OPS / 1e12, 3), "unit": "TOP/s",
-                     "frac": round(achieved / VALU_PEAK_OPS, 4), "traffic": None,
+                     "frac": round(achieved / VALU_PEAK_OPS, 4),
+                     "traffic": hbm["bytes_per_launch"] if hbm else None,
                      "alg_slots_per_mac": ALG_SLOTS_PER_MAC[model], "unit_basis": UNIT_BASIS,
                      "launch_ms_mean": round(1e3 * avg_s, 4),
                      "launch_ms_min": launch_stats(launch_ms)[0],
                      "launch_ms_std": launch_stats(launch_ms)[1]},
         "cpu_baseline": cpu,
     }
+    if valu:
+        out["roofline"]["valu_slots_per_mac"] = valu["valu_slots_per_mac"]
+        out["roofline"]["valu_frac"] = round(
+            valu["valu_slots_per_mac"] * macs / avg_s / VALU_PEAK_OPS, 4)
     print(json.dumps(out), flush=True)
 
 
@@ -506,13 +529,7 @@ def main():
     value = MACS * args.steps / ev_total_s
 
     if args.copy_calibration:
-        src = torch.empty(64 << 20, dtype=torch.int32, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(2):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(dev)
 
     fingerprint_repeats = (bool(torch.equal(tX, X_warm)) if X_warm is not None else None)
     # parity of the timed output against the oracle's full-output digest

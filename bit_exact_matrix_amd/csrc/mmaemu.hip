@@ -446,11 +446,12 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
 template <int MODEL, int DT>
 hipError_t launch_tiles(const void* A, const void* B, const uint32_t* C, uint32_t* D,
                         uint32_t* X, int64_t ntiles, hipStream_t s) {
-  // one wave per four tiles, in a grid-stride loop: 7 waves per CU (the
-  // LDS bound) on 256 CUs, each with several groups of tiles to overlap
-  // its loads with
+  // one wave per two tiles, in a grid-stride loop: as many waves as the
+  // CUs hold at once (tilek::kWavesPerCU on 256 CUs), each with several
+  // groups of tiles to overlap its loads with
   const int64_t groups = (ntiles + tilek::TPW - 1) / tilek::TPW;
-  const int64_t grid = groups < 1792 ? groups : 1792;
+  const int64_t cap = 256 * tilek::kWavesPerCU<MODEL>;
+  const int64_t grid = groups < cap ? groups : cap;
   tilek::tiles_fast_kernel<MODEL, DT>
       <<<dim3((unsigned)grid), dim3(64), 0, s>>>(A, B, C, D, X, ntiles);
   return hipGetLastError();

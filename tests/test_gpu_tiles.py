@@ -1,7 +1,8 @@
 """mma_emulate_tiles at its edges, GPU against the oracle bit for bit:
-batches that end in a partial group of four tiles, C = NULL, C == D on
-adversarial tiles (the exact recompute must read the original C), and C, D
-and the codes at addresses that are not 16-byte aligned (the scalar path)."""
+batches that end in a partial group of tiles, C = NULL, C == D on
+adversarial tiles (the exact recompute must read the original C), C, D
+and the codes at addresses that are not 16-byte aligned (the scalar path),
+and batches that follow a GEMM which left the LDS full of its own data."""
 import numpy as np
 import pytest
 
@@ -158,3 +159,25 @@ def test_cancelling_inf_nan_products(torch_dev, orc, model, dt, variant):
                       to_dev(torch_dev, Ct), xorsum=True)
     assert_bits_equal(to_host_bits(Dt), wt, f"cancelling specials tiles {model}/{dt}")
     assert_bits_equal(to_host_bits(Xt), wtx, f"cancelling specials tiles {model}/{dt} xorsum")
+
+
+@pytest.mark.parametrize("model,dt", COMBOS)
+def test_tiles_after_a_gemm_left_lds_dirty(torch_dev, orc, model, dt):
+    """Tile batches run right after a tiled GEMM on the same stream, whose
+    operand images leave the LDS full of non-zero words: every LDS word the
+    tile kernel reads must be one it wrote in this group of tiles (a stage
+    word left partly unwritten would pick up the GEMM's data)."""
+    import os
+    os.environ["MMAEMU_NARROW_BLOCKS"] = "0"
+    try:
+        for n in (3, 66, 700):
+            Ag, Bg, Cg = I.gemm_normal(9800 + n, 512, 512, 256, I.FP16, c_zero=False)
+            mm.gemm("ampere", "fp16", to_dev(torch_dev, Ag), to_dev(torch_dev, Bg),
+                    to_dev(torch_dev, Cg))
+            A, B, C = _batch(9900 + n, n, dt)
+            say("tiles after a GEMM", model, dt, n)
+            D, X = mm.tiles(model, dt, to_dev(torch_dev, A), to_dev(torch_dev, B),
+                            to_dev(torch_dev, C), xorsum=True)
+            _check(torch_dev, model, dt, A, B, C, D, X, orc, f"tiles after gemm {model}/{dt} n={n}")
+    finally:
+        del os.environ["MMAEMU_NARROW_BLOCKS"]
