@@ -726,7 +726,11 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
     int64_t M, int64_t N, int64_t K, int64_t s00, int64_t ns,
     const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b, int64_t i0,
     int64_t istride, int64_t zstride, const int32_t* __restrict__ order) {
-  __shared__ Stage stage[2];
+  // the two stages of the double buffer are two LDS variables, not one
+  // array: the compiler can then tell that the copy into one (a
+  // global->LDS load, counted in vmcnt) cannot alias the reads of the
+  // other, and does not wait for the copy before the step that overlaps it
+  __shared__ Stage stage0, stage1;
   const int64_t z = blockIdx.z;
   const uint32_t* const C = z ? nullptr : C0;
   const int64_t s0 = s00 + z * ns;
@@ -761,23 +765,23 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
   uint32_t ca[4], cb[4];
   // fill of stage s (local step s, absolute step s0 + s): start it (before
   // the previous step's compute), end it
-  auto begin_fill = [&](int64_t s) {
+  auto begin_fill = [&](Stage* st, int64_t s) {
     if constexpr (DMA) {
-      dma_step(&stage[s & 1], img_a + s * IMG_WORDS, img_b + s * IMG_WORDS, w, lane);
+      dma_step(st, img_a + s * IMG_WORDS, img_b + s * IMG_WORDS, w, lane);
     } else {
       fetch<DT>(A, B, M, N, K, bm, bn, step_at(order, s0 + s, K / 16), t, ca, cb);
     }
   };
-  auto end_fill = [&](int64_t s) {
+  auto end_fill = [&](Stage* st) {
     if constexpr (DMA) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     } else {
-      produce<MODEL, DT>(&stage[s & 1], ca, cb, t);
+      produce<MODEL, DT>(st, ca, cb, t);
     }
   };
   if (nsteps > 0) {
-    begin_fill(0);
-    end_fill(0);
+    begin_fill(&stage0, 0);
+    end_fill(&stage0);
   }
   __syncthreads();
 
@@ -788,9 +792,9 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
     };
   };
   for (int64_t s = 0; s < nsteps; s += 2) {
-    if (s + 1 < nsteps) begin_fill(s + 1);
-    tile_step<MODEL, DT>(&stage[s & 1], ty, tx, X, NE, Xn, NEn, redo_at(s0 + s));
-    if (s + 1 < nsteps) end_fill(s + 1);
+    if (s + 1 < nsteps) begin_fill(&stage1, s + 1);
+    tile_step<MODEL, DT>(&stage0, ty, tx, X, NE, Xn, NEn, redo_at(s0 + s));
+    if (s + 1 < nsteps) end_fill(&stage1);
     __syncthreads();
     if (s + 1 >= nsteps) {
 #pragma unroll
@@ -803,9 +807,9 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
         for (int c = 0; c < 4; ++c) NE[q][c] = NEn[q][c];
       break;
     }
-    if (s + 2 < nsteps) begin_fill(s + 2);
-    tile_step<MODEL, DT>(&stage[(s + 1) & 1], ty, tx, Xn, NEn, X, NE, redo_at(s0 + s + 1));
-    if (s + 2 < nsteps) end_fill(s + 2);
+    if (s + 2 < nsteps) begin_fill(&stage0, s + 2);
+    tile_step<MODEL, DT>(&stage1, ty, tx, Xn, NEn, X, NE, redo_at(s0 + s + 1));
+    if (s + 2 < nsteps) end_fill(&stage0);
     __syncthreads();
   }
 
