@@ -1,0 +1,408 @@
+// gemm_spread.h -- the chained GEMM for few outputs and long chains: each
+// output's products are spread over L = 2 or 4 lanes, so that such a GEMM
+// still runs several waves per SIMD.  With one lane per output (the narrow
+// kernel) a 256 x 256 output fills one wave per SIMD, and each K-step is a
+// long chain of dependent instructions of that one wave.  Same arithmetic as
+// gemm_fast.h and gemm_narrow.h:
+//
+//  * a pre-pass (spread_unpack_kernel) decodes every row of A and column of
+//    B at every chain position into a 160-byte image: 16 significands (A
+//    pre-shifted onto the group grid, B signed), 16 sign masks and the 16
+//    exponent codes in pairs over consecutive k.  Bits 24-31 of each
+//    significand word carry the signs of the 8 codes of its group of 8 k:
+//    v_mad_i32_i24 ignores those bits;
+//  * the kernel copies the images of its tile's rows and columns into one of
+//    eight LDS stages with direct global->LDS loads, seven positions ahead;
+//  * lane h of an output's L lanes takes products k in [h*NK, (h+1)*NK) of
+//    each group (NK = group size / L).  The group's maximum exponent is the
+//    minimum of the lanes' exponent codes (two DPP steps at most), and the
+//    exact group sum is the sum of the lanes' exact partial sums (integer
+//    addition: associative, and every term is truncated before it is added).
+//    Every lane of the output keeps the same state; lane 0 alone adds the
+//    state's (or the Ampere stage-1 sum's) term and writes the result.
+#pragma once
+
+#include "gemm_narrow.h"
+
+namespace mmaemu {
+namespace spreadk {
+
+using namespace fastk;
+
+constexpr int IW = 40;   // words of one row's (column's) image at one position
+constexpr int TC = 16;   // tile columns; tile rows TR<L> = 16 / L
+constexpr int NSTAGE = 8;  // LDS stages: positions in flight
+template <int L>
+constexpr int TR = 16 / L;
+
+// Image rows and columns are padded to whole tiles (the padding reads the
+// code of 1.0, as in the tiled kernel's images).
+template <int L>
+inline int64_t spread_rows(int64_t M) {
+  return (M + TR<L> - 1) / TR<L> * TR<L>;
+}
+inline int64_t spread_cols(int64_t N) { return (N + TC - 1) / TC * TC; }
+// Workspace bytes of the images of one chain position.
+template <int L>
+inline int64_t spread_step_bytes(int64_t M, int64_t N) {
+  return (spread_rows<L>(M) + spread_cols(N)) * IW * 4;
+}
+
+// Pre-pass: images of chain positions [t0, t0 + gridDim.x) of rows (IS_B
+// false) or columns (IS_B true) [64 * blockIdx.y, ...) of one operand, into
+// ws laid out [position - t0][nimg][IW].  limit: the matrix's rows (columns);
+// image rows past it read the code of 1.0.
+template <int MODEL, int DT, bool IS_B>
+__global__ __launch_bounds__(64) void spread_unpack_kernel(const void* __restrict__ src,
+                                                           int64_t limit, int64_t K, int64_t N,
+                                                           int64_t t0,
+                                                           const int32_t* __restrict__ order,
+                                                           uint32_t* __restrict__ ws,
+                                                           int64_t nimg) {
+  __shared__ uint32_t img[64][IW + 1];
+  const int64_t s = step_at(order, t0 + blockIdx.x, K / 16);
+  const int r = threadIdx.x;
+  const int64_t idx = (int64_t)blockIdx.y * 64 + r;
+  uint32_t val[16], ne[16];
+  int sg[16];
+  uint32_t signs = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    uint32_t code = PAD_CODE<DT>;
+    if (idx < limit)
+      code = IS_B ? load_code<DT>(src, (16 * s + k) * N + idx)
+                  : load_code<DT>(src, idx * K + 16 * s + k);
+    if (IS_B) {
+      image_b<DT>(code, val[k], sg[k], ne[k]);
+    } else {
+      image_a<MODEL, DT>(code, val[k], sg[k], ne[k]);
+    }
+    signs |= (uint32_t)(sg[k] & 1) << k;
+  }
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    img[r][k] = (val[k] & 0x00FFFFFFu) | ((signs >> (8 * (k >> 3))) & 0xFFu) << 24;
+    img[r][16 + k] = (uint32_t)sg[k];
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) img[r][32 + q] = ne[2 * q] | ne[2 * q + 1] << 16;
+  __syncthreads();
+  const int64_t first = (int64_t)blockIdx.y * 64;
+  const int nrows = nimg - first < 64 ? (int)(nimg - first) : 64;
+  uint32_t* dst = ws + ((int64_t)blockIdx.x * nimg + first) * IW;
+  for (int w = r; w < nrows * IW; w += 64) dst[w] = img[w / IW][w % IW];
+}
+
+// One LDS stage: the TR images of the tile's rows, then its TC columns'
+// (3840 or 3200 bytes), in whole 1 KiB wave copies.
+struct alignas(16) SStage {
+  uint32_t w[1024];
+};
+
+// A workgroup barrier without the fences of __syncthreads, whose release
+// half would wait for every global->LDS copy in flight: the empty asm
+// statements keep the compiler from moving memory operations across it,
+// and the waits the stages need are explicit (each wave waits for its own
+// copies before it arrives; every LDS read a step makes is consumed, so
+// complete, before its wave reaches the next barrier).
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// 16 bytes per lane from src to LDS at lds + 16 * lane (lds wave-uniform):
+// one global->LDS load, written out so that the compiler does not track
+// it.  It would otherwise wait for every copy in flight before any read of
+// the stage array, not knowing which stage a copy writes; here the waits
+// for the copies are explicit (s_waitcnt before stage_barrier), and the
+// memory clobber keeps LDS accesses on their side of the statement.  The
+// instruction writes no register, so nothing the compiler allocates can
+// change under it while it is in flight.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds)
+      : "memory", "m0");
+}
+
+// n consecutive LDS words from p, which is aligned to 4 n bytes (n = 1, 2
+// or a multiple of 4): b128 / b64 / b32 reads.
+template <int n>
+__device__ __forceinline__ void lds_words(const uint32_t* p, uint32_t (&v)[n]) {
+  if constexpr (n % 4 == 0) {
+#pragma unroll
+    for (int j = 0; j < n / 4; ++j) {
+      const uint4 x = ((const uint4*)p)[j];
+      v[4 * j] = x.x, v[4 * j + 1] = x.y, v[4 * j + 2] = x.z, v[4 * j + 3] = x.w;
+    }
+  } else if constexpr (n == 2) {
+    const uint2 x = *(const uint2*)p;
+    v[0] = x.x, v[1] = x.y;
+  } else {
+    v[0] = p[0];
+  }
+}
+
+template <int L>
+__device__ __forceinline__ uint32_t across(uint32_t x, bool sum) {
+  // the L lanes of an output are consecutive lanes of one quad
+  uint32_t y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+  x = sum ? x + y : (x < y ? x : y);
+  if constexpr (L == 4) {
+    y = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xF, 0xF, true);  // lane ^ 2
+    x = sum ? x + y : (x < y ? x : y);
+  }
+  return x;
+}
+
+// This lane's share of one group of its output: NK products with
+// significands av/bv, sign masks as/bs and exponent-code pairs ae/be, plus
+// the extra term (X_own, ne_t): X_own is the term's significand in lane 0
+// and 0 in the other lanes.  negbits: the lane's negative products.
+// Returns the exact group sum (the same in all L lanes) on the grid of the
+// group's largest exponent, whose code is mn_out.
+template <int L, int NK, bool NT_EMPTY>
+__device__ __forceinline__ int spread_group(const uint32_t (&av)[NK], const int (&as)[NK],
+                                            const int (&bv)[NK], const int (&bs)[NK],
+                                            const uint32_t (&ae)[NK / 2],
+                                            const uint32_t (&be)[NK / 2], uint32_t ne_t,
+                                            int X_own, uint32_t negbits, uint32_t& mn_out) {
+  constexpr int NP = NK / 2;
+  u16x2 e[NP];
+#pragma unroll
+  for (int p = 0; p < NP; ++p) e[p] = as2(ae[p]) + as2(be[p]);
+  u16x2 m = splat_lo(ne_t);
+  int p = 0;
+  if constexpr (NT_EMPTY) {  // the code 0xFFFF (empty sum) is a binary16 NaN pattern
+    m = __builtin_elementwise_min(m, e[0]);
+    p = 1;
+  }
+  for (; p + 1 < NP; p += 2) m = min3h(m, e[p], e[p + 1]);
+  if (p < NP) m = min3h(m, e[p], e[p]);
+  m = __builtin_elementwise_min(m, u16x2{m.y, m.x});  // both halves: the lane's minimum
+  const uint32_t mm = across<L>(as32(m), false);     // both halves: the group's
+  m = as2(mm);
+  const u16x2 Kc = u16x2{SAT, SAT} - m;
+  const uint32_t wt = as32(__builtin_elementwise_add_sat(splat_lo(ne_t), Kc));
+  int acc = X_own >> (wt & 31);
+#pragma unroll
+  for (int q = 0; q < NP; ++q) {
+    const uint32_t w = as32(__builtin_elementwise_add_sat(e[q], Kc));
+    const int x0 = __mul24(bv[2 * q], (int)av[2 * q]) + bs[2 * q];
+    const int x1 = __mul24(bv[2 * q + 1], (int)av[2 * q + 1]) + bs[2 * q + 1];
+    acc = xad(x0 >> (w & 31), as[2 * q], acc);
+    acc = xad(x1 >> ((w >> 16) & 31), as[2 * q + 1], acc);
+  }
+  acc += __popc(negbits | ((uint32_t)X_own & 0x80000000u));
+  mn_out = mm & 0xFFFFu;
+  return (int)across<L>((uint32_t)acc, true);
+}
+
+// Chains the ns chain positions that start at s0 for the TR x 16 output tile
+// (blockIdx.y, blockIdx.x), from C (NULL: +0), into the sink; position p
+// applies K-step step_at(order, p), whose images sit at position p - i0 of
+// ws_a ([.][ma][IW]) and ws_b ([.][nb][IW]).
+template <int MODEL, int DT, int L>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gemm_spread_kernel(
+    const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
+    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns, const int32_t* __restrict__ order,
+    const uint32_t* __restrict__ ws_a, const uint32_t* __restrict__ ws_b, int64_t ma,
+    int64_t nb, int64_t i0) {
+  constexpr int F = Model<MODEL>::F;
+  constexpr int G = MODEL == kAmpere ? 8 : 16;  // group size
+  constexpr int NG = 16 / G;
+  constexpr int NK = G / L;  // products per lane and group
+  constexpr int R = TR<L>;
+  __shared__ SStage stg[NSTAGE];
+  const int64_t T = K / 16;
+  const int tid = threadIdx.x, h = tid & (L - 1), o = tid / L;
+  const int c = o % TC, r = o / TC;
+  const int64_t row = (int64_t)blockIdx.y * R + r, col = (int64_t)blockIdx.x * TC + c;
+  const bool live = row < M && col < N;
+
+  // the copy: wave w moves stage bytes [1024 w, 1024 w + 1024), lane l the
+  // 16 bytes at 1024 w + 16 l: a piece of a row image, of a column image, or
+  // (past both) a second copy of the tile's first row image, never read
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int boff = 1024 * w + 16 * lane;
+  const bool in_a = boff < R * IW * 4, in_b = !in_a && boff < (R + TC) * IW * 4;
+  const char* const lane_src =
+      in_b ? (const char*)(ws_b + (int64_t)blockIdx.x * TC * IW) + (boff - R * IW * 4)
+           : (const char*)(ws_a + (int64_t)blockIdx.y * R * IW) + (in_a ? boff : 0);
+  const int64_t lane_stride = (in_b ? nb : ma) * IW * 4;  // bytes per position
+  auto copy = [&](SStage* st, int64_t t) {
+    const int64_t p = s0 + (t < ns ? t : ns - 1) - i0;
+    copy16_to_lds(lane_src + p * lane_stride,
+                  (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(st->w + 256 * w));
+  };
+
+  int X;
+  uint32_t NE;
+  bits_to_state<MODEL>((C && live) ? C[row * N + col] : 0u, X, NE);
+  const int own = h == 0 ? -1 : 0;
+  // this lane's products: k in [g*G + h*NK, g*G + (h+1)*NK) of group g; their
+  // sign bits sit at bit 24 + (h*NK mod 8) of the group's significand words
+  const int k_lane = h * NK, neg_at = 24 + (h * NK) % 8;
+  const int ia = r * IW, ib = (R + c) * IW;
+
+  auto step = [&](const SStage* st, int64_t t) {
+    const uint32_t* const pa = st->w + ia;
+    const uint32_t* const pb = st->w + ib;
+    uint32_t av[NG][NK], as_[NG][NK], bv_[NG][NK], bs_[NG][NK], ae[NG][NK / 2], be[NG][NK / 2];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const int k0 = g * G + k_lane;
+      lds_words<NK>(pa + k0, av[g]);
+      lds_words<NK>(pa + 16 + k0, as_[g]);
+      lds_words<NK>(pb + k0, bv_[g]);
+      lds_words<NK>(pb + 16 + k0, bs_[g]);
+      lds_words<NK / 2>(pa + 32 + k0 / 2, ae[g]);
+      lds_words<NK / 2>(pb + 32 + k0 / 2, be[g]);
+    }
+    // every read in flight before the arithmetic starts: one LDS round trip
+    __builtin_amdgcn_sched_barrier(0);
+    int as[NG][NK], bv[NG][NK], bs[NG][NK];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int q = 0; q < NK; ++q) {
+        as[g][q] = (int)as_[g][q];
+        bv[g][q] = (int)bv_[g][q];
+        bs[g][q] = (int)bs_[g][q];
+      }
+    uint32_t negb[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      negb[g] = __builtin_amdgcn_ubfe(av[g][0] ^ (uint32_t)bv[g][0], neg_at, NK);
+
+    int Xn;
+    uint32_t NEn, mn;
+    if (MODEL == kAmpere) {
+      const int S1 = spread_group<L, NK, false>(av[0], as[0], bv[0], bs[0], ae[0], be[0], NE,
+                                                X & own, negb[0], mn);
+      int X1;
+      uint32_t NE1;
+      narrowk::normalise1<0, F>(S1, mn, X1, NE1);
+      // inf/NaN terms in stage 1 may cancel to S1 = 0, which stage 2 would
+      // take for an empty sum: keep their exponent, so that the result
+      // lands out of range and the step is recomputed exactly
+      if (mn <= SPECIAL_MAX) NE1 = mn;
+      const int S = spread_group<L, NK, true>(av[NG - 1], as[NG - 1], bv[NG - 1], bs[NG - 1],
+                                              ae[NG - 1], be[NG - 1], NE1, X1 & own,
+                                              negb[NG - 1], mn);
+      narrowk::normalise1<F - 23, F>(S, mn, Xn, NEn);
+    } else {
+      const int S = spread_group<L, NK, false>(av[0], as[0], bv[0], bs[0], ae[0], be[0], NE,
+                                               X & own, negb[0], mn);
+      narrowk::normalise1<F - 23, F>(S, mn, Xn, NEn);
+    }
+    const bool bad = (uint32_t)((NEn - NE_OK_LO) & 0xFFFFu) > NE_OK_SPAN;
+    // FP32 overflow (L >= 128): the state becomes inf (see tile_step)
+    if (DT == kBF16) {
+      NEn = NEn <= NE_OVF ? C_INF : NEn;
+    } else {
+      NEn = NEn < NE_OVF ? NE_OVF : NEn;
+    }
+    if (bad && live) {
+      // every lane of the output recomputes it, so that all keep the state
+      const uint2 rr = narrowk::redo_step<MODEL, DT>(A, B, N, K, step_at(order, s0 + t, T),
+                                                    row, col, X, NE);
+      Xn = (int)rr.x;
+      NEn = rr.y;
+    }
+    X = Xn;
+    NE = NEn;
+  };
+  auto stage = [&](int u) -> SStage* { return &stg[u]; };
+  // s_waitcnt vmcnt(n): the copies this wave issued, all but its last n,
+  // have landed (lgkm and exp counts not waited for)
+  constexpr int kWaitAllButLast2 = 0xF70 | (NSTAGE - 2);
+
+  // Whole passes of NSTAGE positions with no exit inside (an exit path back
+  // to the loop head would make every copy wait for all the others), then
+  // the last ns % NSTAGE positions from the stages already being filled.
+  // Each wave waits for its own copies before the barrier, after which every
+  // wave reads the stage; the stage a copy refills was read at the step
+  // before, which every wave has left at this barrier.
+  if (ns > 0) {
+    const int64_t nfull = ns - ns % NSTAGE;
+#pragma unroll
+    for (int u = 0; u + 1 < NSTAGE; ++u) copy(stage(u), u);
+    for (int64_t t0 = 0; t0 < nfull; t0 += NSTAGE) {
+#pragma unroll
+      for (int u = 0; u < NSTAGE; ++u) {
+        __builtin_amdgcn_s_waitcnt(kWaitAllButLast2);
+        stage_barrier();
+        copy(stage((u + NSTAGE - 1) % NSTAGE), t0 + u + NSTAGE - 1);
+        step(stage(u), t0 + u);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u + 1 < NSTAGE; ++u) {
+      if (nfull + u < ns) {
+        __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+        stage_barrier();
+        step(stage(u), nfull + u);
+      }
+    }
+  }
+
+  const uint32_t d = state_to_bits<MODEL>(X, NE);
+  uint32_t x = 0, nbad = 0;
+  unsigned long long first = ~0ull;
+  if (live && h == 0) {
+    const int64_t idx = row * N + col;
+    if (out.claimed) {
+      x = d ^ out.claimed[idx];
+      if (x) {
+        nbad = 1;
+        first = (unsigned long long)idx;
+      }
+    } else {
+      x = out.accumulate ? fp32_add_rne(out.D[idx], d) : d;
+      out.D[idx] = x;
+    }
+  }
+  if (out.claimed) report_mismatches(out.report, nbad, first);
+  if (out.xorsum) {
+    // XOR across the TC * L consecutive lanes of the tile row (32 or 64)
+#pragma unroll
+    for (int off = TC * L / 2; off >= 1; off >>= 1) x ^= __shfl_xor(x, off, TC * L);
+    if ((tid & (TC * L - 1)) == 0 && row < M && x) atomicXor(&out.xorsum[row], x);
+  }
+}
+
+// The spread chain of a plain GEMM (emulation or the audit compare).  ws
+// holds the images of ws_steps positions (spread_step_bytes each); when that
+// is fewer than all K/16, an emulating call runs the chain in chunks of
+// ws_steps positions, each restarting from the D the chunk before wrote
+// (every step's result is an FP32 value, so the chain through D is the same
+// chain).  The caller makes sure the audit compare gets all positions.
+template <int MODEL, int DT, int L>
+inline void gemm_spread_launch(const void* A, const void* B, const uint32_t* C,
+                               const Sink& out, int64_t M, int64_t N, int64_t K, void* ws,
+                               int64_t ws_steps, hipStream_t s, const int32_t* order) {
+  const int64_t ma = spread_rows<L>(M), nb = spread_cols(N), T = K / 16;
+  uint32_t* const ws_a = (uint32_t*)ws;
+  uint32_t* const ws_b = ws_a + ws_steps * ma * IW;
+  const dim3 grid((unsigned)(nb / TC), (unsigned)(ma / TR<L>));
+  for (int64_t t0 = 0; t0 < T; t0 += ws_steps) {
+    const int64_t n = T - t0 < ws_steps ? T - t0 : ws_steps;
+    spread_unpack_kernel<MODEL, DT, false>
+        <<<dim3((unsigned)n, (unsigned)((ma + 63) / 64)), dim3(64), 0, s>>>(A, M, K, N, t0,
+                                                                           order, ws_a, ma);
+    spread_unpack_kernel<MODEL, DT, true>
+        <<<dim3((unsigned)n, (unsigned)((nb + 63) / 64)), dim3(64), 0, s>>>(B, N, K, N, t0,
+                                                                           order, ws_b, nb);
+    Sink o = out;
+    if (t0 + n < T) o.xorsum = nullptr;
+    gemm_spread_kernel<MODEL, DT, L><<<grid, dim3(256), 0, s>>>(
+        A, B, t0 == 0 ? C : out.D, o, M, N, K, t0, n, order, ws_a, ws_b, ma, nb, t0);
+  }
+}
+
+}  // namespace spreadk
+}  // namespace mmaemu

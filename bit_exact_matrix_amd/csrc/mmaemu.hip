@@ -13,6 +13,7 @@
 #include "mmaemu_common.h"
 #include "gemm_fast.h"
 #include "gemm_narrow.h"
+#include "gemm_spread.h"
 #include "tiles_fast.h"
 
 using namespace mmaemu;
@@ -349,8 +350,52 @@ bool takes_narrow(int64_t M, int64_t N, int64_t K, int64_t splits) {
   return nb_env >= 0 ? M * N / 4096 < nb_env : narrow_is_faster(M, N);
 }
 
+// MMAEMU_SPREAD_LANES, read on every call: 0 never runs the spread kernel,
+// 2 or 4 runs it with that many lanes per output wherever the narrow kernel
+// would run; -1 when it is not set (or set to anything else).
+int spread_env() {
+  const char* v = getenv("MMAEMU_SPREAD_LANES");
+  if (v && (!strcmp(v, "0") || !strcmp(v, "2") || !strcmp(v, "4"))) return atoi(v);
+  return -1;
+}
+
+// Lanes per output of the spread kernel for a chain that the narrow kernel
+// would take (0: the narrow kernel itself).  The narrow kernel runs four
+// waves per 16 x 16 tile; at two waves per SIMD or fewer (2048 waves on the
+// 256 CUs) its SIMDs mostly wait on the dependent instructions of one
+// wave's step, and two lanes per output (twice the waves, half the products
+// per lane) win: measured on MI355X, 256 x 256 x 65536 FP16 Ampere 3.33 ->
+// 2.15 ms, 48 x 48 x 65536 3.23 -> 1.40 ms, 128 x 1024 x 16384 1.12 ->
+// 1.00 ms (E4M3 Hopper 3.17 -> 1.94, 3.15 -> 1.09 and 1.07 -> 0.86 ms);
+// at 4096 waves (512 x 512) the two are even, beyond it the narrow kernel
+// wins.  Four lanes (4-row tiles) while that still makes at most one wave
+// per SIMD: a lone wave's step is shorter with four products per lane than
+// with eight (48 x 48 x 65536 E4M3 Hopper 1.40 -> 1.09 ms).
+int spread_lanes(int64_t M, int64_t N) {
+  const int e = spread_env();
+  if (e >= 0) return e;
+  const int64_t waves = 4 * ((M + 15) / 16) * ((N + 15) / 16);
+  if (waves > 2048) return 0;
+  return 4 * ((M + 3) / 4) * ((N + 15) / 16) <= 1024 ? 4 : 2;
+}
+
+// The spread kernel's grids: (N / 16, rows / (16 / L)) and the pre-pass's
+// (positions, images / 64).
+bool spread_supported(int64_t M, int64_t N, int L) {
+  return (M + 3) / 4 <= 65535 && (M + 63) / 64 <= 65535 && (N + 63) / 64 <= 65535 &&
+         (L == 2 || L == 4);
+}
+
+template <int MODEL, int DT, int L>
+void spread_launch(const void* A, const void* B, const uint32_t* C, const Sink& out,
+                   int64_t M, int64_t N, int64_t K, void* ws, int64_t ws_steps, hipStream_t s,
+                   const int32_t* order) {
+  spreadk::gemm_spread_launch<MODEL, DT, L>(A, B, C, out, M, N, K, ws, ws_steps, s, order);
+}
+
 // The workspace one K-step of a plain chain needs on the kernel the
-// library picks for it: the operand images of the tiled kernel, else 0.
+// library picks for it: the operand images of the tiled kernel, else 0 (the
+// narrow kernel needs none, and the spread kernel falls back to it).
 int64_t chain_step_bytes(int64_t M, int64_t N, int64_t K, const Sink& out) {
   if (M == 0 || N == 0) return 0;
   if (row_slices(M, N, K, 1, out)) return gemm_fast_workspace_bytes(kSliceRows, N, 16);
@@ -383,6 +428,30 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
   if (out.report) init_report_kernel<<<dim3(1), dim3(64), 0, s>>>(out.report);
   if (M == 0 || N == 0) return hipGetLastError();
   if (takes_narrow(M, N, K, splits)) {
+    // the spread kernel when the workspace holds its images (all K-steps'
+    // for the audit compare, which cannot restart from D), else the narrow one
+    const int L = spread_lanes(M, N);
+    if (L && spread_supported(M, N, L)) {
+      const int64_t T = K / 16;
+      const int64_t step_bytes = L == 2 ? spreadk::spread_step_bytes<2>(M, N)
+                                        : spreadk::spread_step_bytes<4>(M, N);
+      const bool fixed = sch.ws.fixed != nullptr;
+      const int64_t cap = fixed ? sch.ws.fixed_bytes : workspace_cap();
+      int64_t ws_steps = cap / step_bytes < T ? cap / step_bytes : T;
+      if (ws_steps < T && (out.claimed || out.accumulate || !out.D)) ws_steps = 0;
+      void* ws = nullptr;
+      if (ws_steps > 0) ws = fixed ? sch.ws.fixed : workspace_alloc(ws_steps * step_bytes, s);
+      if (ws) {
+        if (L == 2) {
+          spread_launch<MODEL, DT, 2>(A, B, C, out, M, N, K, ws, ws_steps, s, order);
+        } else {
+          spread_launch<MODEL, DT, 4>(A, B, C, out, M, N, K, ws, ws_steps, s, order);
+        }
+        const hipError_t e = hipGetLastError();
+        if (!fixed) (void)hipFreeAsync(ws, s);
+        return e;
+      }
+    }
     narrowk::gemm_narrow_kernel<MODEL, DT>
         <<<dim3((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), dim3(256), 0, s>>>(
             A, B, C, out, M, N, K, 0, K / 16, order);

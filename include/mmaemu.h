@@ -60,17 +60,29 @@
  *   KERNEL CHOICE.  A plain chain runs on a kernel with one lane per
  *   output, which needs no workspace, when an estimate of both kernels'
  *   time says it is the faster (small M * N, or a few rows against a wide
- *   N).  Shapes over 1,048,560 rows always run on the other kernels, and a
- *   plain GEMM over 4,194,240 rows runs in row slices of that height.
- *   Whichever kernels run, the results are the same.
+ *   N).  Where that kernel would leave the GPU mostly idle (at most 2048
+ *   waves: few outputs, typically with a long K), the chain instead runs
+ *   on a kernel that spreads each output over 2 or 4 lanes; its own
+ *   pre-pass stages 160 bytes per K-step for each row of A and each column
+ *   of B (rows padded to 4 or 8, columns to 16) in the same kind of
+ *   workspace, under the same cap and in the same chunks; an audit compare
+ *   whose images do not all fit, or a call whose allocation fails, takes
+ *   the one-lane kernel.  Shapes over 1,048,560 rows always run on the
+ *   tiled kernels, and a plain GEMM over 4,194,240 rows runs in row slices
+ *   of that height.  Whichever kernels run, the results are the same.
  *   DIAGNOSTIC OVERRIDES.  Nothing needs to be set in the environment.
- *   Three variables, read on every call and without effect when unset,
+ *   Four variables, read on every call and without effect when unset,
  *   force the schedules above so that each can be tested on any shape:
  *   MMAEMU_WORKSPACE_MAX_BYTES (a byte count) replaces the 1 GiB cap;
- *   MMAEMU_NO_WORKSPACE (set to anything) stages every operand in LDS;
+ *   MMAEMU_NO_WORKSPACE (set to anything) stages every operand of the
+ *   tiled kernel in LDS (and leaves the spread kernel none: the one-lane
+ *   kernel runs instead);
  *   MMAEMU_NARROW_BLOCKS replaces the kernel estimate by a threshold: the
- *   one-lane-per-output kernel below that many units of 4096 outputs
- *   (M * N), 0 never.  None of them changes a result.
+ *   one-lane-per-output kernels below that many units of 4096 outputs
+ *   (M * N), 0 never;
+ *   MMAEMU_SPREAD_LANES (0, 2 or 4) decides, where a one-lane-per-output
+ *   kernel runs, between the one-lane kernel (0) and the spread kernel
+ *   with that many lanes per output.  None of them changes a result.
  *   A  M x K row-major raw codes: uint16 (FP16, BF16) or uint8 (E4M3)
  *   B  K x N row-major raw codes, same type
  *   C  M x N row-major FP32 (read as bit patterns); NULL means all +0.0

@@ -23,14 +23,17 @@ from test_gpu_parity import assert_bits_equal, run_gemm, say, torch_dev  # noqa:
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["tiled", "tiled-in-lds", "narrow"])
+@pytest.fixture(params=["tiled", "tiled-in-lds", "narrow", "spread"])
 def kernel(request):
-    """The three operand decoders: the tiled kernel's pre-pass (operand
+    """The four operand decoders: the tiled kernel's pre-pass (operand
     images in a workspace), its in-LDS image builder (no workspace; the
-    tile batches use the same builder), and the narrow kernel's own."""
+    tile batches use the same builder), the narrow kernel's own and the
+    spread kernel's pre-pass (one image per row or column)."""
     env = {"tiled": {"MMAEMU_NARROW_BLOCKS": "0"},
            "tiled-in-lds": {"MMAEMU_NARROW_BLOCKS": "0", "MMAEMU_NO_WORKSPACE": "1"},
-           "narrow": {"MMAEMU_NARROW_BLOCKS": str(1 << 40)}}[request.param]
+           "narrow": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "0"},
+           "spread": {"MMAEMU_NARROW_BLOCKS": str(1 << 40),
+                      "MMAEMU_SPREAD_LANES": "2"}}[request.param]
     os.environ.update(env)
     yield request.param
     for k in env:

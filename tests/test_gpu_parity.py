@@ -248,16 +248,29 @@ def no_workspace():
     del os.environ["MMAEMU_NARROW_BLOCKS"]
 
 
-@pytest.fixture(params=["tiled", "narrow"])
+# MMAEMU_NARROW_BLOCKS replaces the library's kernel estimate by a
+# block-count threshold (0: never the narrow kernel, a huge value: always,
+# where it applies); MMAEMU_SPREAD_LANES then picks the narrow kernel itself
+# (0) or the spread kernel with 2 or 4 lanes per output.
+KERNEL_ENV = {
+    "tiled": {"MMAEMU_NARROW_BLOCKS": "0"},
+    "narrow": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "0"},
+    "spread2": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "2"},
+    "spread4": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "4"},
+}
+
+
+@pytest.fixture(params=list(KERNEL_ENV))
 def gemm_kernel(request):
     """Run a test once on each GEMM kernel: the tiled one (4x4 outputs per
-    lane) and the narrow one (one output per lane), which the library takes
-    for plain chains where it estimates it the faster.  MMAEMU_NARROW_BLOCKS
-    replaces the estimate by a block-count threshold: 0 never takes the
-    narrow kernel, a huge value always (where it applies)."""
-    os.environ["MMAEMU_NARROW_BLOCKS"] = "0" if request.param == "tiled" else str(1 << 40)
+    lane), the narrow one (one output per lane) and the spread one (each
+    output over 2 or 4 lanes), the last two of which the library takes for
+    plain chains where it estimates them the faster."""
+    env = KERNEL_ENV[request.param]
+    os.environ.update(env)
     yield request.param
-    del os.environ["MMAEMU_NARROW_BLOCKS"]
+    for k in env:
+        del os.environ[k]
 
 
 @pytest.mark.parametrize("model,dt", COMBOS)

@@ -131,13 +131,15 @@ def _cancelling_specials(model, dt, n_rows, seed):
 
 @pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("ampere", "bf16"),
                                       ("hopper", "fp16")])
-@pytest.mark.parametrize("variant", ["tiled", "tiled-no-workspace", "narrow"])
+@pytest.mark.parametrize("variant", ["tiled", "tiled-no-workspace", "narrow", "spread2",
+                                     "spread4"])
 def test_cancelling_inf_nan_products(torch_dev, orc, model, dt, variant):
     import os
     A, B, C = _cancelling_specials(model, dt, 64, 9950)
     want, wx = orc.gemm(model, dt, A, B, C)
     assert np.all(want == 0x7FC00000), "the construction must give NaN everywhere"
-    os.environ["MMAEMU_NARROW_BLOCKS"] = str(1 << 40) if variant == "narrow" else "0"
+    os.environ["MMAEMU_NARROW_BLOCKS"] = "0" if variant.startswith("tiled") else str(1 << 40)
+    os.environ["MMAEMU_SPREAD_LANES"] = {"spread2": "2", "spread4": "4"}.get(variant, "0")
     if variant == "tiled-no-workspace":
         os.environ["MMAEMU_NO_WORKSPACE"] = "1"
     try:
@@ -147,6 +149,7 @@ def test_cancelling_inf_nan_products(torch_dev, orc, model, dt, variant):
         got, gx = to_host_bits(D), to_host_bits(X)
     finally:
         del os.environ["MMAEMU_NARROW_BLOCKS"]
+        del os.environ["MMAEMU_SPREAD_LANES"]
         os.environ.pop("MMAEMU_NO_WORKSPACE", None)
     assert_bits_equal(got, want, f"cancelling specials {model}/{dt}/{variant}")
     assert_bits_equal(gx, wx, f"cancelling specials {model}/{dt}/{variant} xorsum")
