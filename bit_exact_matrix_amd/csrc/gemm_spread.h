@@ -63,15 +63,40 @@ __global__ __launch_bounds__(64) void spread_unpack_kernel(const void* __restric
   const int64_t s = step_at(order, t0 + blockIdx.x, K / 16);
   const int r = threadIdx.x;
   const int64_t idx = (int64_t)blockIdx.y * 64 + r;
+  uint32_t codes[16];
+  // an A row segment is 16 consecutive codes: two (E4M3: one) 16-byte loads
+  // when rows start 16-byte aligned
+  constexpr int esz = Fmt<DT>::bytes;
+  const bool vec = !IS_B && idx < limit && (((uintptr_t)src | (uintptr_t)(K * esz)) & 15u) == 0;
+  if (vec) {
+    const uint4* p = (const uint4*)((const char*)src + (idx * K + 16 * s) * esz);
+    uint32_t w[8];
+    const uint4 v0 = p[0];
+    w[0] = v0.x, w[1] = v0.y, w[2] = v0.z, w[3] = v0.w;
+    if constexpr (esz == 2) {
+      const uint4 v1 = p[1];
+      w[4] = v1.x, w[5] = v1.y, w[6] = v1.z, w[7] = v1.w;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) codes[k] = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) codes[k] = (w[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      codes[k] = PAD_CODE<DT>;
+      if (idx < limit)
+        codes[k] = IS_B ? load_code<DT>(src, (16 * s + k) * N + idx)
+                        : load_code<DT>(src, idx * K + 16 * s + k);
+    }
+  }
   uint32_t val[16], ne[16];
   int sg[16];
   uint32_t signs = 0;
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
-    uint32_t code = PAD_CODE<DT>;
-    if (idx < limit)
-      code = IS_B ? load_code<DT>(src, (16 * s + k) * N + idx)
-                  : load_code<DT>(src, idx * K + 16 * s + k);
+    const uint32_t code = codes[k];
     if (IS_B) {
       image_b<DT>(code, val[k], sg[k], ne[k]);
     } else {

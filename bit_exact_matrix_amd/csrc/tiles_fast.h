@@ -49,9 +49,9 @@ constexpr int SW = 16 * TPW;  // stage rows (columns)
 // fourteen per CU; Hopper's keeps all 16 product exponents of a group live
 // and fits three per SIMD (168 VGPRs).
 template <int MODEL>
-constexpr int kWavesPerSimd = MODEL == kAmpere ? 4 : 3;
+constexpr int kWavesPerSimd = 3;
 template <int MODEL>
-constexpr int kWavesPerCU = MODEL == kAmpere ? 14 : 12;
+constexpr int kWavesPerCU = 12;
 
 // One operand's stage: [k][stage row (A) or column (B)].  The writers are
 // one lane per row (column) and k, the readers read two or four
@@ -431,9 +431,44 @@ __device__ __forceinline__ void tile_step_pair(const ST* st, int pr, int pc,
   }
 }
 
+// The codes and C words of group g on the fast path (A, C and D 16-byte
+// aligned, C present): the same loads for every group, tiles past the end
+// reading the last tile again (their outputs are never stored), so that
+// the compiler can count the loads in flight and wait for exactly one
+// group's.
+template <int DT>
+__device__ __forceinline__ void load_group(const void* A, const void* B, const uint32_t* C,
+                                           int64_t g, int64_t ntiles, int L, int u, int q,
+                                           int b, uint32_t (&ra)[4], uint32_t (&rb)[8],
+                                           uint32_t (&cb)[2][4]) {
+  const int r = L & (SW - 1), h = L / SW;
+  const int64_t last = ntiles - 1;
+  const int64_t tc = TPW * g + r / 16 < last ? TPW * g + r / 16 : last;
+  const int64_t ia = tc * 256 + 16 * (r & 15) + 8 * h, ib = tc * 256 + 128 * h + (r & 15);
+  if (Fmt<DT>::bytes == 2) {
+    const uint4 v = *(const uint4*)((const uint16_t*)A + ia);
+    ra[0] = v.x, ra[1] = v.y, ra[2] = v.z, ra[3] = v.w;
+  } else {
+    const uint2 v = *(const uint2*)((const uint8_t*)A + ia);
+    ra[0] = v.x, ra[1] = v.y, ra[2] = 0, ra[3] = 0;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) rb[k] = load_code<DT>(B, ib + 16 * k);
+  const int64_t tu = TPW * g + u < last ? TPW * g + u : last;
+  const int64_t ic = tu * 256 + 32 * q + 4 * b;
+#pragma unroll
+  for (int rr = 0; rr < 2; ++rr) {
+    const uint4 x = *(const uint4*)(C + ic + 16 * rr);
+    cb[rr][0] = x.x, cb[rr][1] = x.y, cb[rr][2] = x.z, cb[rr][3] = x.w;
+  }
+}
+
 // One wave per two tiles at a time, in a grid-stride loop.  Its 64 lanes:
 // lane (u, q, b) = (lane / 32, lane / 4 % 8, lane % 4) owns rows 2q, 2q+1
-// and columns 4b .. 4b+3 of tile u of the pair.
+// and columns 4b .. 4b+3 of tile u of the pair.  On the fast path (see
+// load_group) the next group's codes and C words are loaded while this
+// group computes (two register sets, the loop unrolled twice); otherwise
+// each group's loads start its iteration.
 template <int MODEL, int DT>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<MODEL>))) void
 tiles_fast_kernel(
@@ -450,9 +485,8 @@ tiles_fast_kernel(
   // their exact recompute reads
   const bool inplace = (const void*)C == (const void*)D;
 
-  uint32_t ra[4], rb[8], cbits[2][4];
   // the C words of the lane's outputs (output (2q + r, 4b + c) of tile u)
-  auto load_c = [&](int64_t g) {
+  auto load_c = [&](int64_t g, uint32_t (&cbits)[2][4]) {
     const int64_t tile = TPW * g + u;
     const int64_t ic = tile * 256 + 32 * q + 4 * b;
     if (C && vec && TPW * g + TPW <= ntiles) {
@@ -470,16 +504,13 @@ tiles_fast_kernel(
         for (int c = 0; c < 4; ++c) cbits[r][c] = live ? C[ic + 16 * r + c] : 0u;
     }
   };
-  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+  // group g from its codes and C words
+  auto body = [&](int64_t g, const uint32_t (&ra)[4], const uint32_t (&rb)[8],
+                  const uint32_t (&cbits)[2][4]) {
     // an opaque copy of the lane index, so that the compiler recomputes the
     // staging addresses here instead of keeping them live across the loop
     int sl = lane;
     asm volatile("" : "+v"(sl));
-    // this group's codes and C words; the latency is hidden by the other
-    // waves of the SIMD (three or four), not by registers held across the
-    // step
-    load_codes<DT>(A, B, TPW * g, ntiles, sl, avec, ra, rb);
-    load_c(g);
     wave_sync();  // the previous tiles' LDS reads come first
     {
       uint32_t wa[4], wb[4];
@@ -544,6 +575,35 @@ tiles_fast_kernel(
       xs = row16_xor(xs);
       xs ^= from_next_row16(xs);
       if ((lane & 31) == 0 && live) xorsum[tile] = xs;
+    }
+  };
+
+  int64_t g = blockIdx.x;
+  if (vec && avec && C) {
+    if (g >= ngroups) return;
+    uint32_t ra0[4], rb0[8], cb0[2][4], ra1[4], rb1[8], cb1[2][4];
+    load_group<DT>(A, B, C, g, ntiles, lane, u, q, b, ra0, rb0, cb0);
+    for (;;) {
+      load_group<DT>(A, B, C, g + gridDim.x, ntiles, lane, u, q, b, ra1, rb1, cb1);
+      body(g, ra0, rb0, cb0);
+      g += gridDim.x;
+      if (g >= ngroups) break;
+      load_group<DT>(A, B, C, g + gridDim.x, ntiles, lane, u, q, b, ra0, rb0, cb0);
+      body(g, ra1, rb1, cb1);
+      g += gridDim.x;
+      if (g >= ngroups) break;
+    }
+  } else {
+    for (; g < ngroups; g += gridDim.x) {
+      // this group's codes and C words; the latency is hidden by the other
+      // waves of the SIMD (three or four), not by registers held across the
+      // step
+      uint32_t ra[4], rb[8], cbits[2][4];
+      int sl = lane;
+      asm volatile("" : "+v"(sl));
+      load_codes<DT>(A, B, TPW * g, ntiles, sl, avec, ra, rb);
+      load_c(g, cbits);
+      body(g, ra, rb, cbits);
     }
   }
 }
