@@ -23,6 +23,8 @@
 //    outside the matrix skip that (their result is never stored).
 #pragma once
 
+#include <type_traits>
+
 #include "gemm_fast.h"
 
 namespace mmaemu {
@@ -44,6 +46,38 @@ struct alignas(16) NStage {
   uint32_t am[16];      // sign bitmasks over k: rows
   uint32_t bm[4][16];   // columns, one slice of k per wave
 };
+
+// The stage when A comes from row images (AIMG): the tile's 16 row images
+// as a pre-pass wrote them (the spread kernel's layout: 16 significands with
+// their group's sign byte in bits 24-31, 16 sign masks, 8 exponent-code
+// pairs), copied in three 1 KiB pieces (the last one half padding), then
+// B as above.
+constexpr int AIW = 40;
+struct alignas(16) NStageA {
+  uint32_t a[16][AIW];
+  uint32_t pad_[768 - 16 * AIW];
+  uint32_t bv[16][RP];
+  int bs[16][RP];
+  uint32_t be[16][EP];
+  uint32_t bm[4][16];
+};
+
+// 16 bytes per lane from src to LDS at lds + 16 * lane (lds wave-uniform):
+// one global->LDS load, written out so that the compiler does not track
+// it (it would wait for every copy in flight before any read of the stage
+// array, or, behind a workgroup barrier's release fence, for all of them
+// before the barrier); the waits for the copies are explicit.  The memory
+// clobber keeps LDS accesses on their side of the statement, and the
+// instruction writes no register, so nothing the compiler allocates can
+// change under it while it is in flight.
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds)
+      : "memory", "m0");
+}
 
 // One group of the lane's output: products k in [2*p0, 2*(p0+NP)), the extra
 // term (X_t, ne_t).  Returns the exact signed group sum on the grid of the
@@ -116,13 +150,21 @@ __device__ __noinline__ uint2 redo_step(const void* A, const void* B, int64_t N,
 // (blockIdx.y, blockIdx.x), from C (NULL: +0), into the sink; position p
 // applies K-step step_at(order, p).  Compiled for four waves per SIMD (128
 // VGPRs).
-template <int MODEL, int DT>
+// AIMG: A comes from row images of positions [i0, ...) in ws_a (laid out
+// [position - i0][ma][AIW], ma = M rounded up to 16, as the spread
+// kernel's pre-pass writes them): the A image of step t + 1 is copied into
+// LDS while step t computes, instead of every workgroup of a row of tiles
+// decoding the same A codes again.  Otherwise each lane decodes one A code
+// per step, as it does one B code.
+template <int MODEL, int DT, bool AIMG = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void gemm_narrow_kernel(
     const void* __restrict__ A, const void* __restrict__ B, const uint32_t* C, Sink out,
-    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns, const int32_t* __restrict__ order) {
+    int64_t M, int64_t N, int64_t K, int64_t s0, int64_t ns, const int32_t* __restrict__ order,
+    const uint32_t* __restrict__ ws_a = nullptr, int64_t ma = 0, int64_t i0 = 0) {
   constexpr int F = Model<MODEL>::F;
   const int64_t T = K / 16;
-  __shared__ NStage stage[2];
+  using Stage = typename std::conditional<AIMG, NStageA, NStage>::type;
+  __shared__ Stage stage[2];
   const int tid = threadIdx.x, i = tid >> 4, j = tid & 15, wv = tid >> 6;
   const int64_t row = (int64_t)blockIdx.y * 16 + i, col = (int64_t)blockIdx.x * 16 + j;
   const bool live = row < M && col < N;
@@ -130,26 +172,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
   // codes outside the matrix
   uint32_t ca = 0, cb = 0;
   auto load = [&](int64_t s) {
-    ca = row < M ? load_code<DT>(A, row * K + 16 * s + j) : 0u;
+    if (!AIMG) ca = row < M ? load_code<DT>(A, row * K + 16 * s + j) : 0u;
     cb = col < N ? load_code<DT>(B, (16 * s + i) * N + col) : 0u;
+  };
+  // AIMG: wave w < 3 copies bytes [1024 w, 1024 w + 1024) of the tile's row
+  // images of position s0 + t; lanes past the 2560 bytes re-read its start
+  // into the padding
+  const int w = __builtin_amdgcn_readfirstlane(wv), lane = tid & 63;
+  const int aoff = 1024 * w + 16 * lane;
+  const char* const a_src = AIMG ? (const char*)(ws_a + (int64_t)blockIdx.y * 16 * AIW) +
+                                       (aoff < 16 * AIW * 4 ? aoff : 0)
+                                 : nullptr;
+  auto copy_a = [&](Stage* st, int64_t t) {
+    if constexpr (AIMG) {
+      if (w < 3)
+        copy16_to_lds(a_src + (s0 + t - i0) * ma * AIW * 4,
+                      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)(
+                          &st->a[0][0] + 256 * w));
+    }
   };
 
   int X;
   uint32_t NE;
   bits_to_state<MODEL>((C && live) ? C[row * N + col] : 0u, X, NE);
-  if (ns > 0) load(step_at(order, s0, T));
+  if (ns > 0) {
+    load(step_at(order, s0, T));
+    copy_a(&stage[0], 0);
+  }
   for (int64_t t = 0; t < ns; ++t) {
-    NStage* st = &stage[t & 1];
+    Stage* st = &stage[t & 1];
     {
       uint32_t v, ne;
       int s;
-      image_a<MODEL, DT>(ca, v, s, ne);
-      st->av[i][j] = v;
-      st->as[i][j] = s;
-      const uint32_t ne_a1 = from_lane_xor1(ne);  // the same row's code at k ^ 1
-      if ((j & 1) == 0) st->ae[i][j >> 1] = ne | ne_a1 << 16;
-      const uint64_t bal_a = __ballot(s != 0);       // bit 16*(i&3) + k: row i's signs
-      if (j == 0) st->am[i] = (uint32_t)(bal_a >> (16 * (i & 3))) & 0xFFFFu;
+      if constexpr (!AIMG) {
+        image_a<MODEL, DT>(ca, v, s, ne);
+        st->av[i][j] = v;
+        st->as[i][j] = s;
+        const uint32_t ne_a1 = from_lane_xor1(ne);  // the same row's code at k ^ 1
+        if ((j & 1) == 0) st->ae[i][j >> 1] = ne | ne_a1 << 16;
+        const uint64_t bal_a = __ballot(s != 0);       // bit 16*(i&3) + k: row i's signs
+        if (j == 0) st->am[i] = (uint32_t)(bal_a >> (16 * (i & 3))) & 0xFFFFu;
+      }
 
       image_b<DT>(cb, v, s, ne);
       st->bv[j][i] = v;
@@ -167,14 +230,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
       }
     }
     if (t + 1 < ns) load(step_at(order, s0 + t + 1, T));
+    if constexpr (AIMG) {
+      // this step's A copy (started at the step before) has landed: all but
+      // the one B code load issued since.  Each wave waits for its own copy
+      // before the barrier, after which every wave reads the whole image.
+      __builtin_amdgcn_s_waitcnt(0xF71);  // vmcnt(1)
+    }
     __syncthreads();
+    // the next step's A image goes to the other stage, which every wave has
+    // finished reading (its last reader was the step before this barrier)
+    if (t + 1 < ns) copy_a(&stage[(t + 1) & 1], t + 1);
 
     uint32_t av[16], ae[8], be[8];
     int as[16], bv[16], bs[16];
+    const uint32_t* const ar = AIMG ? &((const NStageA*)st)->a[i][0] : nullptr;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const uint4 a4 = *(const uint4*)&st->av[i][4 * q];
-      const int4 sa4 = *(const int4*)&st->as[i][4 * q];
+      uint4 a4;
+      int4 sa4;
+      if constexpr (AIMG) {
+        a4 = *(const uint4*)&ar[4 * q];
+        sa4 = *(const int4*)&ar[16 + 4 * q];
+      } else {
+        a4 = *(const uint4*)&((const NStage*)st)->av[i][4 * q];
+        sa4 = *(const int4*)&((const NStage*)st)->as[i][4 * q];
+      }
       const int4 b4 = *(const int4*)&st->bv[j][4 * q];
       const int4 sb4 = *(const int4*)&st->bs[j][4 * q];
       av[4 * q] = a4.x, av[4 * q + 1] = a4.y, av[4 * q + 2] = a4.z, av[4 * q + 3] = a4.w;
@@ -184,12 +264,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
     }
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
-      const uint4 x = *(const uint4*)&st->ae[i][4 * q];
+      uint4 x;
+      if constexpr (AIMG) {
+        x = *(const uint4*)&ar[32 + 4 * q];
+      } else {
+        x = *(const uint4*)&((const NStage*)st)->ae[i][4 * q];
+      }
       const uint4 y = *(const uint4*)&st->be[j][4 * q];
       ae[4 * q] = x.x, ae[4 * q + 1] = x.y, ae[4 * q + 2] = x.z, ae[4 * q + 3] = x.w;
       be[4 * q] = y.x, be[4 * q + 1] = y.y, be[4 * q + 2] = y.z, be[4 * q + 3] = y.w;
     }
-    const uint32_t neg = st->am[i] ^ (st->bm[0][j] | st->bm[1][j] | st->bm[2][j] | st->bm[3][j]);
+    // the row's sign bits: from the images' sign bytes (k = 0..7 on the word
+    // of k = 0, k = 8..15 on that of k = 8), or the staged bitmask
+    uint32_t am;
+    if constexpr (AIMG) {
+      am = (av[0] >> 24) | (av[8] >> 24) << 8;
+    } else {
+      am = ((const NStage*)st)->am[i];
+    }
+    const uint32_t neg = am ^ (st->bm[0][j] | st->bm[1][j] | st->bm[2][j] | st->bm[3][j]);
 
     int Xn;
     uint32_t NEn, mn;

@@ -452,9 +452,30 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
         return e;
       }
     }
-    narrowk::gemm_narrow_kernel<MODEL, DT>
-        <<<dim3((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16)), dim3(256), 0, s>>>(
-            A, B, C, out, M, N, K, 0, K / 16, order);
+    const dim3 grid((unsigned)((N + 15) / 16), (unsigned)((M + 15) / 16));
+    {
+      // the narrow kernel with A from row images (the spread kernel's
+      // pre-pass, rows padded to 16) when the workspace holds all K-steps'
+      const int64_t T = K / 16, ma = (M + 15) / 16 * 16;
+      const int64_t bytes = ma * spreadk::IW * 4 * T;
+      const bool fixed = sch.ws.fixed != nullptr;
+      const int64_t cap = fixed ? sch.ws.fixed_bytes : workspace_cap();
+      void* ws = nullptr;
+      if (bytes <= cap && (ma + 63) / 64 <= 65535)
+        ws = fixed ? sch.ws.fixed : workspace_alloc(bytes, s);
+      if (ws) {
+        spreadk::spread_unpack_kernel<MODEL, DT, false>
+            <<<dim3((unsigned)T, (unsigned)((ma + 63) / 64)), dim3(64), 0, s>>>(
+                A, M, K, N, 0, order, (uint32_t*)ws, ma);
+        narrowk::gemm_narrow_kernel<MODEL, DT, true><<<grid, dim3(256), 0, s>>>(
+            A, B, C, out, M, N, K, 0, T, order, (const uint32_t*)ws, ma, 0);
+        const hipError_t e = hipGetLastError();
+        if (!fixed) (void)hipFreeAsync(ws, s);
+        return e;
+      }
+    }
+    narrowk::gemm_narrow_kernel<MODEL, DT><<<grid, dim3(256), 0, s>>>(A, B, C, out, M, N, K, 0,
+                                                                     K / 16, order);
     return hipGetLastError();
   }
   if (gemm_fast_supported(M, N, K)) {

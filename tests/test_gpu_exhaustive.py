@@ -23,15 +23,18 @@ from test_gpu_parity import assert_bits_equal, run_gemm, say, torch_dev  # noqa:
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture(params=["tiled", "tiled-in-lds", "narrow", "spread"])
+@pytest.fixture(params=["tiled", "tiled-in-lds", "narrow", "narrow-lds", "spread"])
 def kernel(request):
-    """The four operand decoders: the tiled kernel's pre-pass (operand
-    images in a workspace), its in-LDS image builder (no workspace; the
-    tile batches use the same builder), the narrow kernel's own and the
-    spread kernel's pre-pass (one image per row or column)."""
+    """The operand decoders: the tiled kernel's pre-pass (operand images in
+    a workspace), its in-LDS image builder (no workspace; the tile batches
+    use the same builder), the narrow kernel's own (B always; A without a
+    workspace) and the spread kernel's pre-pass (one image per row or
+    column; also the narrow kernel's A when there is a workspace)."""
     env = {"tiled": {"MMAEMU_NARROW_BLOCKS": "0"},
            "tiled-in-lds": {"MMAEMU_NARROW_BLOCKS": "0", "MMAEMU_NO_WORKSPACE": "1"},
            "narrow": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "0"},
+           "narrow-lds": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "0",
+                          "MMAEMU_NO_WORKSPACE": "1"},
            "spread": {"MMAEMU_NARROW_BLOCKS": str(1 << 40),
                       "MMAEMU_SPREAD_LANES": "2"}}[request.param]
     os.environ.update(env)

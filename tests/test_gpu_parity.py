@@ -255,6 +255,10 @@ def no_workspace():
 KERNEL_ENV = {
     "tiled": {"MMAEMU_NARROW_BLOCKS": "0"},
     "narrow": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "0"},
+    # no workspace: the narrow kernel decodes A itself instead of copying
+    # the pre-pass's row images
+    "narrow-lds": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "0",
+                   "MMAEMU_NO_WORKSPACE": "1"},
     "spread2": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "2"},
     "spread4": {"MMAEMU_NARROW_BLOCKS": str(1 << 40), "MMAEMU_SPREAD_LANES": "4"},
 }

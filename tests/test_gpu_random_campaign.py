@@ -29,8 +29,8 @@ pytestmark = pytest.mark.gpu
 COMBOS = [("ampere", "fp16"), ("hopper", "fp16"), ("ampere", "bf16"), ("hopper", "bf16"),
           ("hopper", "e4m3"), ("lovelace", "fp16")]
 RECIPES = ["wide", "narrow", "coarse", "tiny", "specials", "normal"]
-PATHS = ["tiled", "tiled-in-lds", "narrow", "spread2", "spread4", "splitk", "ordered", "verify",
-         "tiles"]
+PATHS = ["tiled", "tiled-in-lds", "narrow", "narrow-lds", "spread2", "spread4", "splitk",
+         "ordered", "verify", "tiles"]
 ENV = ("MMAEMU_NARROW_BLOCKS", "MMAEMU_NO_WORKSPACE", "MMAEMU_SPREAD_LANES")
 # shape bounds: M, N below MAX_MN, K up to 16 * MAX_STEPS
 MAX_MN = int(os.environ.get("MMAEMU_CAMPAIGN_MAX_MN", "300"))
@@ -42,11 +42,11 @@ def _set_path(path):
         os.environ.pop(k, None)
     if path in ("tiled", "tiled-in-lds"):
         os.environ["MMAEMU_NARROW_BLOCKS"] = "0"
-    if path == "tiled-in-lds":
+    if path in ("tiled-in-lds", "narrow-lds"):
         os.environ["MMAEMU_NO_WORKSPACE"] = "1"
-    if path in ("narrow", "spread2", "spread4"):
+    if path in ("narrow", "narrow-lds", "spread2", "spread4"):
         os.environ["MMAEMU_NARROW_BLOCKS"] = str(1 << 40)
-        os.environ["MMAEMU_SPREAD_LANES"] = {"narrow": "0", "spread2": "2", "spread4": "4"}[path]
+        os.environ["MMAEMU_SPREAD_LANES"] = {"spread2": "2", "spread4": "4"}.get(path, "0")
 
 
 def _gemm_inputs(seed, recipe, dt, M, N, K):
@@ -100,7 +100,8 @@ def _one_case(torch_dev, orc, case):
         ok = mm.mismatches(report) == want[:2] and np.array_equal(to_host_bits(X), want[2])
         return None if ok else what
     if path == "ordered":
-        kernel = ("tiled", "tiled-in-lds", "narrow", "spread2", "spread4")[rng.integers(5)]
+        kernel = ("tiled", "tiled-in-lds", "narrow", "narrow-lds", "spread2",
+                  "spread4")[rng.integers(6)]
         _set_path(kernel)
         order = rng.permutation(T)
         if rng.integers(4) == 0:

@@ -131,8 +131,8 @@ def _cancelling_specials(model, dt, n_rows, seed):
 
 @pytest.mark.parametrize("model,dt", [("ampere", "fp16"), ("ampere", "bf16"),
                                       ("hopper", "fp16")])
-@pytest.mark.parametrize("variant", ["tiled", "tiled-no-workspace", "narrow", "spread2",
-                                     "spread4"])
+@pytest.mark.parametrize("variant", ["tiled", "tiled-no-workspace", "narrow", "narrow-lds",
+                                     "spread2", "spread4"])
 def test_cancelling_inf_nan_products(torch_dev, orc, model, dt, variant):
     import os
     A, B, C = _cancelling_specials(model, dt, 64, 9950)
@@ -140,7 +140,7 @@ def test_cancelling_inf_nan_products(torch_dev, orc, model, dt, variant):
     assert np.all(want == 0x7FC00000), "the construction must give NaN everywhere"
     os.environ["MMAEMU_NARROW_BLOCKS"] = "0" if variant.startswith("tiled") else str(1 << 40)
     os.environ["MMAEMU_SPREAD_LANES"] = {"spread2": "2", "spread4": "4"}.get(variant, "0")
-    if variant == "tiled-no-workspace":
+    if variant in ("tiled-no-workspace", "narrow-lds"):
         os.environ["MMAEMU_NO_WORKSPACE"] = "1"
     try:
         say("cancelling inf/NaN products", model, dt, variant)

@@ -54,8 +54,9 @@ def test_noalloc_full_size_then_smaller(torch_dev):
 
 
 def test_noalloc_small_shapes_in_a_row(torch_dev):
-    """A tiled-kernel shape with specials, then a narrow-kernel shape (no
-    scratch), then a smaller tiled one, each against the pooled call."""
+    """A tiled-kernel shape with specials, then a few-output shape (the
+    spread kernel, its images in the scratch), then a smaller tiled one,
+    each against the pooled call."""
     for model, dt, (M, N, K), kind in (("hopper", "e4m3", (300, 260, 640), "specials"),
                                        ("ampere", "fp16", (3, 900, 256), "normal"),
                                        ("ampere", "bf16", (130, 100, 160), "specials")):
@@ -63,6 +64,22 @@ def test_noalloc_small_shapes_in_a_row(torch_dev):
         say("no-alloc", model, dt, (M, N, K))
         (d1, x1), (d2, x2) = _both(torch_dev, model, dt, A, B, C)
         assert np.array_equal(d1, d2) and np.array_equal(x1, x2), (model, dt, M, N, K)
+
+
+def test_noalloc_spread_chain_in_chunks(torch_dev):
+    """256 x 256 x 65536 on the spread kernel: its images take 80 KiB per
+    position, so the 64 MiB scratch holds 819 of the 4096 positions and the
+    chain runs in five chunks through D, where the pooled call holds them
+    all; then a smaller few-output GEMM on the same scratch."""
+    from bit_exact_matrix_amd import inputs as I
+    A, B, C = I.gemm_normal(15400, 256, 256, 65536, I.FP16, c_zero=False)
+    say("no-alloc spread 256x256x65536")
+    (d1, x1), (d2, x2) = _both(torch_dev, "ampere", "fp16", A, B, C)
+    assert np.array_equal(d1, d2) and np.array_equal(x1, x2)
+    A, B, C = _gen("specials", "hopper", "e4m3", 40, 50, 1024, 15500)
+    say("no-alloc spread 40x50x1024 after it")
+    (d1, x1), (d2, x2) = _both(torch_dev, "hopper", "e4m3", A, B, C)
+    assert np.array_equal(d1, d2) and np.array_equal(x1, x2)
 
 
 def test_noalloc_rejects_a_shape_beyond_its_scratch(torch_dev):
