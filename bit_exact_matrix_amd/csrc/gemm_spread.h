@@ -28,6 +28,7 @@ namespace mmaemu {
 namespace spreadk {
 
 using namespace fastk;
+using narrowk::copy16_to_lds;  // the stages' global->LDS copies
 
 constexpr int IW = 40;   // words of one row's (column's) image at one position
 constexpr int TC = 16;   // tile columns; tile rows TR<L> = 16 / L
@@ -134,23 +135,6 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-}
-
-// 16 bytes per lane from src to LDS at lds + 16 * lane (lds wave-uniform):
-// one global->LDS load, written out so that the compiler does not track
-// it.  It would otherwise wait for every copy in flight before any read of
-// the stage array, not knowing which stage a copy writes; here the waits
-// for the copies are explicit (s_waitcnt before stage_barrier), and the
-// memory clobber keeps LDS accesses on their side of the statement.  The
-// instruction writes no register, so nothing the compiler allocates can
-// change under it while it is in flight.
-__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(src), "s"(lds)
-      : "memory", "m0");
 }
 
 // n consecutive LDS words from p, which is aligned to 4 n bytes (n = 1, 2
