@@ -223,9 +223,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
       // column j's signs at k = 4*wv + r sit in bits 16*r + j of this wave's ballot
       const uint64_t bal_b = __ballot(s != 0);
       if ((i & 3) == 0) {
-        uint32_t c4 = 0;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) c4 |= (uint32_t)((bal_b >> (16 * r + j)) & 1u) << r;
+        // bits j, 16 + j, 32 + j, 48 + j of the ballot, to bits 0..3
+        const uint32_t lo = (uint32_t)bal_b >> j, hi = (uint32_t)(bal_b >> 32) >> j;
+        const uint32_t c4 = (lo & 1u) | (lo >> 15 & 2u) | (hi & 1u) << 2 | (hi >> 13 & 8u);
         st->bm[wv][j] = c4 << (4 * wv);
       }
     }
