@@ -11,7 +11,10 @@
 //    signed, 0/-1 sign masks, 16-bit exponent codes paired over
 //    consecutive k, and per-row / per-column sign bitmasks; B is stored
 //    transposed so that every lane reads both of its operand rows
-//    contiguously over k.  The next step's codes are loaded meanwhile;
+//    contiguously over k.  The next step's codes are loaded meanwhile.
+//    With a workspace, A instead comes as the row images a pre-pass wrote
+//    (gemm_spread.h), copied into the stage while the step before computes,
+//    so that a row of tiles does not decode the same A codes once per tile;
 //  * each lane forms the exponents of two products per packed add, keeps
 //    the group maximum with packed binary16 minimum3, gets both alignment
 //    distances from one saturating packed add, and accumulates each product

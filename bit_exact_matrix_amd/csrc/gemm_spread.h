@@ -10,7 +10,8 @@
 //    pre-shifted onto the group grid, B signed), 16 sign masks and the 16
 //    exponent codes in pairs over consecutive k.  Bits 24-31 of each
 //    significand word carry the signs of the 8 codes of its group of 8 k:
-//    v_mad_i32_i24 ignores those bits;
+//    v_mad_i32_i24 ignores those bits.  The narrow kernel takes its A rows
+//    from the same pre-pass;
 //  * the kernel copies the images of its tile's rows and columns into one of
 //    eight LDS stages with direct global->LDS loads, seven positions ahead;
 //  * lane h of an output's L lanes takes products k in [h*NK, (h+1)*NK) of
