@@ -536,14 +536,22 @@ hipError_t launch_gemm(const void* A, const void* B, const uint32_t* C, const Si
 template <int MODEL, int DT>
 hipError_t launch_tiles(const void* A, const void* B, const uint32_t* C, uint32_t* D,
                         uint32_t* X, int64_t ntiles, hipStream_t s) {
-  // one wave per two tiles, in a grid-stride loop: as many waves as the
-  // CUs hold at once (tilek::kWavesPerCU on 256 CUs), each with several
-  // groups of tiles to overlap its loads with
-  const int64_t groups = (ntiles + tilek::TPW - 1) / tilek::TPW;
-  const int64_t cap = 256 * tilek::kWavesPerCU<MODEL>;
-  const int64_t grid = groups < cap ? groups : cap;
-  tilek::tiles_fast_kernel<MODEL, DT>
-      <<<dim3((unsigned)grid), dim3(64), 0, s>>>(A, B, C, D, X, ntiles);
+  // one wave per two tiles: one workgroup per CU (256 of them), of as
+  // many waves as a CU holds at once, each workgroup sharing out an equal
+  // part of the groups of tiles among its waves.  The kernel counts tiles
+  // in 32 bits: a larger batch runs as launches of 2^30 tiles each, every
+  // tile being independent.
+  const int64_t esz = DT == kE4M3 ? 1 : 2;
+  constexpr int64_t kChunk = int64_t(1) << 30;
+  for (int64_t t = 0; t < ntiles; t += kChunk) {
+    const int64_t n = ntiles - t < kChunk ? ntiles - t : kChunk;
+    const int64_t groups = (n + tilek::TPW - 1) / tilek::TPW;
+    const int64_t grid = groups < 256 ? groups : 256;
+    tilek::tiles_fast_kernel<MODEL, DT>
+        <<<dim3((unsigned)grid), dim3(64 * tilek::kWavesPerCU<MODEL>), 0, s>>>(
+        (const char*)A + t * 256 * esz, (const char*)B + t * 256 * esz, C ? C + t * 256 : nullptr,
+        D + t * 256, X ? X + t : nullptr, (uint32_t)n);
+  }
   return hipGetLastError();
 }
 

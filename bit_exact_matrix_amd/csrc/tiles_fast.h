@@ -21,9 +21,9 @@
 //    one output at a time: each lane walks its own such outputs, so a wave
 //    pays for the largest count on one lane, not for every output slot that
 //    any lane needs;
-//  * a grid-stride loop over the pairs of tiles, with as many waves as the
-//    CUs hold at once: three or four per SIMD, which hide each other's
-//    memory latency.
+//  * one workgroup per CU, of as many waves as it holds at once (three per
+//    SIMD, which hide each other's memory latency), each wave taking the
+//    next pair of tiles of its workgroup's share from a counter in LDS.
 //
 // The stage (10.5 KiB) and the 8-output lane tile keep the registers and
 // LDS of a wave small enough for several waves per SIMD, which the single
@@ -148,21 +148,6 @@ __device__ __forceinline__ void c_to_state2(uint32_t b0, uint32_t b1, int& X0, i
   const uint32_t m1 = (b1 & 0x7FFFFFu) | min(ef1, 1u) << 23;
   X0 = (int)(m0 << (F - 23)) ^ ((int)b0 >> 31);
   X1 = (int)(m1 << (F - 23)) ^ ((int)b1 >> 31);
-}
-
-// FP32 bits of two fast-path results, valid for outputs the step did not
-// flag: a normal result or the inf state (every other state is flagged).
-// E127 = E + 127 clamped to 255 turns the inf state into an all-ones field,
-// and the min clears its fraction.
-template <int MODEL>
-__device__ __forceinline__ void fast_bits2(int X0, int X1, uint32_t NE, uint32_t& d0,
-                                           uint32_t& d1) {
-  constexpr int F = Model<MODEL>::F;
-  const uint32_t e = as32(__builtin_elementwise_min(splat16(T_BIAS + 127) - as2(NE), splat16(255)));
-  const uint32_t f0 = ((uint32_t)(X0 ^ (X0 >> 31)) >> (F - 23)) & 0x7FFFFFu;
-  const uint32_t f1 = ((uint32_t)(X1 ^ (X1 >> 31)) >> (F - 23)) & 0x7FFFFFu;
-  d0 = min((e & 0xFFFFu) << 23 | f0, 0x7F800000u) | ((uint32_t)X0 & 0x80000000u);
-  d1 = min((e >> 16) << 23 | f1, 0x7F800000u) | ((uint32_t)X1 & 0x80000000u);
 }
 
 // The exact step of output (row, col) of a live tile, from its raw codes
@@ -387,14 +372,18 @@ __device__ __forceinline__ void group_pair(const ST* st, int pr, int pc, int p0,
 }
 
 // One MMA step for the lane's 2x4 outputs (stage row pair pr, columns
-// 4pc ..): state (X, NE) in, (Xn, NEn) out, and bit 4r + c of *bad set for
-// each output (r, c) whose fast result is not trustworthy (zero, below
-// FP32's normal range, touched by inf/NaN); its (Xn, NEn) must be ignored.
+// 4pc ..) from the state (X, NE) of their C: d[r][c] gets the FP32 bits of
+// output (r, c), and bit 4r + c of bad is set for each output whose fast
+// result is not trustworthy (zero, below FP32's normal range, touched by
+// inf/NaN), whose d must then be ignored.  A single step leaves nothing to
+// chain, so the final sums go straight to FP32 bits: the leading one at
+// bit 31 (lz places it there), the 23 bits below it the fraction (the
+// truncation to 24 bits), the exponent field E + 127 from the exponent
+// code, clamped to 255 for the inf state, whose fraction the min clears.
 template <int MODEL, int DT, typename ST>
-__device__ __forceinline__ void tile_step_pair(const ST* st, int pr, int pc,
+__device__ __forceinline__ void tile_step_bits(const ST* st, int pr, int pc,
                                                const int (&X)[2][4], const uint32_t (&NE)[4],
-                                               int (&Xn)[2][4], uint32_t (&NEn)[4],
-                                               uint32_t& bad) {
+                                               uint32_t (&d)[2][4], uint32_t& bad) {
   constexpr int F = Model<MODEL>::F;
   int S[2][4];
   uint32_t mn[4];
@@ -414,71 +403,115 @@ __device__ __forceinline__ void tile_step_pair(const ST* st, int pr, int pc,
   bad = 0;
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    normalise2<F - 23, F>(S[0][c], S[1][c], mn[c], Xn[0][c], Xn[1][c], NEn[c]);
-    const uint32_t ne = NEn[c];
+    const int S0 = S[0][c], S1 = S[1][c];
+    const uint32_t m0 = (uint32_t)max(S0, -S0), m1 = (uint32_t)max(S1, -S1);
+    // lz = lz0 | lz1 << 16, as in normalise2
+    const uint32_t lz = ffbh_into_hi(ffbh(m0), m1);
+    const u16x2 base = as2(mn[c]) - u16x2{(unsigned short)(31 - F), (unsigned short)(31 - F)};
+    uint32_t ne = as32(__builtin_elementwise_add_sat(as2(lz), base));
     const u16x2 off = as2(ne) - u16x2{(unsigned short)NE_OK_LO, (unsigned short)NE_OK_LO};
     bad |= (uint32_t)(off.x > NE_OK_SPAN) << c;
     bad |= (uint32_t)(off.y > NE_OK_SPAN) << (4 + c);
-    // FP32 overflow (L >= 128): the inf state (see tile_step)
+    // FP32 overflow (L >= 128): the inf state (see tile_step in gemm_fast.h)
     if (DT == kBF16) {
       const uint32_t lo = (ne & 0xFFFFu) <= NE_OVF ? C_INF : (ne & 0xFFFFu);
       const uint32_t hi = (ne >> 16) <= NE_OVF ? C_INF : (ne >> 16);
-      NEn[c] = lo | hi << 16;
+      ne = lo | hi << 16;
     } else {
-      NEn[c] = as32(__builtin_elementwise_max(
+      ne = as32(__builtin_elementwise_max(
           as2(ne), u16x2{(unsigned short)NE_OVF, (unsigned short)NE_OVF}));
     }
+    const uint32_t e =
+        as32(__builtin_elementwise_min(splat16(T_BIAS + 127) - as2(ne), splat16(255)));
+    const uint32_t f0 = ((m0 << (lz & 31)) >> 8) & 0x7FFFFFu;
+    const uint32_t f1 = ((m1 << ((lz >> 16) & 31)) >> 8) & 0x7FFFFFu;
+    d[0][c] = min((e & 0xFFFFu) << 23 | f0, 0x7F800000u) | ((uint32_t)S0 & 0x80000000u);
+    d[1][c] = min((e >> 16) << 23 | f1, 0x7F800000u) | ((uint32_t)S1 & 0x80000000u);
   }
 }
 
 // The codes and C words of group g on the fast path (A, C and D 16-byte
-// aligned, C present): the same loads for every group, tiles past the end
-// reading the last tile again (their outputs are never stored), so that
-// the compiler can count the loads in flight and wait for exactly one
-// group's.
+// aligned, C present): the same loads for every group, with no per-lane
+// condition, a second tile past the end reading the last tile again (its
+// outputs are never stored).  Each load is a uniform base (the group's
+// first tile) plus a 32-bit lane offset, which keeps the addresses in
+// scalar registers instead of a 64-bit pair per lane and load.
 template <int DT>
 __device__ __forceinline__ void load_group(const void* A, const void* B, const uint32_t* C,
-                                           int64_t g, int64_t ntiles, int L, int u, int q,
+                                           uint32_t g, uint32_t ntiles, int L, int u, int q,
                                            int b, uint32_t (&ra)[4], uint32_t (&rb)[8],
                                            uint32_t (&cb)[2][4]) {
+  constexpr int esz = Fmt<DT>::bytes;
+  // an opaque copy of the lane index: the lane offsets below are recomputed
+  // for every group rather than held (and spilled) across the step
+  asm volatile("" : "+v"(L));
   const int r = L & (SW - 1), h = L / SW;
-  const int64_t last = ntiles - 1;
-  const int64_t tc = TPW * g + r / 16 < last ? TPW * g + r / 16 : last;
-  const int64_t ia = tc * 256 + 16 * (r & 15) + 8 * h, ib = tc * 256 + 128 * h + (r & 15);
-  if (Fmt<DT>::bytes == 2) {
-    const uint4 v = *(const uint4*)((const uint16_t*)A + ia);
+  const uint32_t last = ntiles - 1;
+  const uint32_t t0 = min(TPW * g, last);
+  // tiles t0 .. t0 + dl exist (dl < TPW)
+  const uint32_t dl = min(last - t0, (uint32_t)(TPW - 1));
+  const uint32_t ta = min((uint32_t)r / 16u, dl), tu = min((uint32_t)u, dl);
+  const char* pa = (const char*)A + (size_t)t0 * 256 * esz;
+  const char* pb = (const char*)B + (size_t)t0 * 256 * esz;
+  const uint32_t* pc = C + (size_t)t0 * 256;
+  const uint32_t oa = (256u * ta + 16u * (uint32_t)(r & 15) + 8u * (uint32_t)h) * esz;
+  const uint32_t ob = (256u * ta + 128u * (uint32_t)h + (uint32_t)(r & 15)) * esz;
+  if (esz == 2) {
+    const uint4 v = *(const uint4*)(pa + oa);
     ra[0] = v.x, ra[1] = v.y, ra[2] = v.z, ra[3] = v.w;
   } else {
-    const uint2 v = *(const uint2*)((const uint8_t*)A + ia);
+    const uint2 v = *(const uint2*)(pa + oa);
     ra[0] = v.x, ra[1] = v.y, ra[2] = 0, ra[3] = 0;
   }
 #pragma unroll
-  for (int k = 0; k < 8; ++k) rb[k] = load_code<DT>(B, ib + 16 * k);
-  const int64_t tu = TPW * g + u < last ? TPW * g + u : last;
-  const int64_t ic = tu * 256 + 32 * q + 4 * b;
+  for (int k = 0; k < 8; ++k)
+    rb[k] = esz == 2 ? (uint32_t) * (const uint16_t*)(pb + ob + 32u * k)
+                     : (uint32_t) * (const uint8_t*)(pb + ob + 16u * k);
+  const uint32_t oc = 256u * tu + 32u * (uint32_t)q + 4u * (uint32_t)b;
 #pragma unroll
   for (int rr = 0; rr < 2; ++rr) {
-    const uint4 x = *(const uint4*)(C + ic + 16 * rr);
+    const uint4 x = *(const uint4*)(pc + oc + 16u * rr);
     cb[rr][0] = x.x, cb[rr][1] = x.y, cb[rr][2] = x.z, cb[rr][3] = x.w;
   }
 }
 
-// One wave per two tiles at a time, in a grid-stride loop.  Its 64 lanes:
-// lane (u, q, b) = (lane / 32, lane / 4 % 8, lane % 4) owns rows 2q, 2q+1
-// and columns 4b .. 4b+3 of tile u of the pair.  On the fast path (see
-// load_group) the next group's codes and C words are loaded while this
-// group computes (two register sets, the loop unrolled twice); otherwise
-// each group's loads start its iteration.
+// One wave per two tiles at a time.  A workgroup is the waves one CU
+// holds at once (kWavesPerCU, each with its own stage), and takes an equal
+// share of the groups of tiles; its waves take the next group of that
+// share from a counter in LDS whenever they start one.  The SIMD issues
+// from its oldest wave first, so waves with equal fixed shares finish far
+// apart (measured: 60 to 140 us for 16 or 17 groups each), leaving the
+// SIMDs with one wave at the end; taken from a counter, the share keeps
+// every wave busy until it is used up.  Its 64 lanes: lane (u, q, b) =
+// (lane / 32, lane / 4 % 8, lane % 4) owns rows 2q, 2q+1 and columns 4b ..
+// 4b+3 of tile u of the pair.  Each group's loads start its iteration; the
+// other waves of the SIMD hide their latency.  (Loading the next group
+// while this one computes, in a second register set, was no faster once
+// the groups were shared out this way: a slow wave then also holds the
+// next group back from the others.)
 template <int MODEL, int DT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<MODEL>))) void
-tiles_fast_kernel(
+__global__ __launch_bounds__(64 * kWavesPerCU<MODEL>) __attribute__((
+    amdgpu_waves_per_eu(kWavesPerSimd<MODEL>))) void tiles_fast_kernel(
     const void* __restrict__ A, const void* __restrict__ B,
     const uint32_t* C,  // may equal D
-    uint32_t* D, uint32_t* __restrict__ xorsum, int64_t ntiles) {
-  __shared__ TileStage st;
-  const int lane = threadIdx.x;
+    uint32_t* D, uint32_t* __restrict__ xorsum, uint32_t ntiles) {
+  __shared__ TileStage stages[kWavesPerCU<MODEL>];
+  __shared__ uint32_t next_group;
+  const int lane = threadIdx.x & 63;
+  TileStage& st = stages[__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)];
   const int u = lane / 32, q = (lane >> 2) & 7, b = lane & 3;
-  const int64_t ngroups = (ntiles + TPW - 1) / TPW;
+  const uint32_t ngroups = (ntiles + TPW - 1) / TPW;
+  // this workgroup's share of the groups: [g_lo, g_hi)
+  const uint32_t g_lo = (uint32_t)((uint64_t)blockIdx.x * ngroups / gridDim.x);
+  const uint32_t g_hi = (uint32_t)((uint64_t)(blockIdx.x + 1) * ngroups / gridDim.x);
+  if (threadIdx.x == 0) next_group = g_lo;
+  __syncthreads();
+  // the next group of the share (g_hi or beyond once it is used up)
+  auto take = [&]() -> uint32_t {
+    uint32_t v = 0;
+    if (lane == 0) v = atomicAdd(&next_group, 1u);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
   const bool vec = (((uintptr_t)C | (uintptr_t)D) & 15u) == 0;
   const bool avec = ((uintptr_t)A & 15u) == 0;
   // in place: the fast results of flagged outputs must not overwrite the C
@@ -486,7 +519,7 @@ tiles_fast_kernel(
   const bool inplace = (const void*)C == (const void*)D;
 
   // the C words of the lane's outputs (output (2q + r, 4b + c) of tile u)
-  auto load_c = [&](int64_t g, uint32_t (&cbits)[2][4]) {
+  auto load_c = [&](uint32_t g, uint32_t (&cbits)[2][4]) {
     const int64_t tile = TPW * g + u;
     const int64_t ic = tile * 256 + 32 * q + 4 * b;
     if (C && vec && TPW * g + TPW <= ntiles) {
@@ -505,7 +538,7 @@ tiles_fast_kernel(
     }
   };
   // group g from its codes and C words
-  auto body = [&](int64_t g, const uint32_t (&ra)[4], const uint32_t (&rb)[8],
+  auto body = [&](uint32_t g, const uint32_t (&ra)[4], const uint32_t (&rb)[8],
                   const uint32_t (&cbits)[2][4]) {
     // an opaque copy of the lane index, so that the compiler recomputes the
     // staging addresses here instead of keeping them live across the loop
@@ -519,22 +552,21 @@ tiles_fast_kernel(
     }
     wave_sync();
 
-    const int64_t tile = TPW * g + u;
-    const bool live = tile < ntiles;
-    // output (2q + r, 4b + c) of the tile sits at base + 16 r + c
-    const int64_t base = tile * 256 + 32 * q + 4 * b;
-    int X[2][4], Xn[2][4];
-    uint32_t NE[4], NEn[4];
+    const uint32_t tg = TPW * g, tile = tg + u;
+    const bool live = (uint32_t)u < ntiles - tg;
+    // output (2q + r, 4b + c) of the tile sits at Dg[od + 16 r + c]: a
+    // uniform base and a 32-bit lane offset
+    uint32_t* const Dg = D + (size_t)tg * 256;
+    const uint32_t od = 256u * (uint32_t)u + 32u * (uint32_t)q + 4u * (uint32_t)b;
+    int X[2][4];
+    uint32_t NE[4];
 #pragma unroll
     for (int c = 0; c < 4; ++c)
       c_to_state2<MODEL>(cbits[0][c], cbits[1][c], X[0][c], X[1][c], NE[c]);
-    uint32_t bad;
-    tile_step_pair<MODEL, DT>(&st, 8 * u + q, 4 * u + b, X, NE, Xn, NEn, bad);
+    uint32_t bad, xs = 0, d[2][4];
+    tile_step_bits<MODEL, DT>(&st, 8 * u + q, 4 * u + b, X, NE, d, bad);
     if (!live) bad = 0;
     // the fast results, 0 in the outputs flagged in bad
-    uint32_t xs = 0, d[2][4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) fast_bits2<MODEL>(Xn[0][c], Xn[1][c], NEn[c], d[0][c], d[1][c]);
 #pragma unroll
     for (int r = 0; r < 2; ++r)
 #pragma unroll
@@ -548,10 +580,10 @@ tiles_fast_kernel(
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           if (vec) {
-            *(uint4*)(D + base + 16 * r) = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
+            *(uint4*)(Dg + od + 16u * r) = make_uint4(d[r][0], d[r][1], d[r][2], d[r][3]);
           } else {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) D[base + 16 * r + c] = d[r][c];
+            for (int c = 0; c < 4; ++c) Dg[od + 16u * r + c] = d[r][c];
           }
         }
       } else {
@@ -559,7 +591,7 @@ tiles_fast_kernel(
         for (int r = 0; r < 2; ++r)
 #pragma unroll
           for (int c = 0; c < 4; ++c)
-            if (!((bad >> (4 * r + c)) & 1u)) D[base + 16 * r + c] = d[r][c];
+            if (!((bad >> (4 * r + c)) & 1u)) Dg[od + 16u * r + c] = d[r][c];
       }
     }
     // the flagged ones, exactly, one per lane at a time
@@ -567,7 +599,7 @@ tiles_fast_kernel(
       const int i = __builtin_ctz(m);
       const int r = i >> 2, c = i & 3;
       const uint32_t v = redo_output<MODEL, DT>(A, B, C, tile, 2 * q + r, 4 * b + c);
-      D[base + 16 * r + c] = v;
+      Dg[od + 16u * r + c] = v;
       xs ^= v;
     }
     if (xorsum) {
@@ -578,26 +610,16 @@ tiles_fast_kernel(
     }
   };
 
-  int64_t g = blockIdx.x;
   if (vec && avec && C) {
-    if (g >= ngroups) return;
-    uint32_t ra0[4], rb0[8], cb0[2][4], ra1[4], rb1[8], cb1[2][4];
-    load_group<DT>(A, B, C, g, ntiles, lane, u, q, b, ra0, rb0, cb0);
-    for (;;) {
-      load_group<DT>(A, B, C, g + gridDim.x, ntiles, lane, u, q, b, ra1, rb1, cb1);
-      body(g, ra0, rb0, cb0);
-      g += gridDim.x;
-      if (g >= ngroups) break;
-      load_group<DT>(A, B, C, g + gridDim.x, ntiles, lane, u, q, b, ra0, rb0, cb0);
-      body(g, ra1, rb1, cb1);
-      g += gridDim.x;
-      if (g >= ngroups) break;
+    for (uint32_t g = take(); g < g_hi; g = take()) {
+      uint32_t ra[4], rb[8], cbits[2][4];
+      load_group<DT>(A, B, C, g, ntiles, lane, u, q, b, ra, rb, cbits);
+      body(g, ra, rb, cbits);
     }
   } else {
-    for (; g < ngroups; g += gridDim.x) {
+    for (uint32_t g = take(); g < g_hi; g = take()) {
       // this group's codes and C words; the latency is hidden by the other
-      // waves of the SIMD (three or four), not by registers held across the
-      // step
+      // waves of the SIMD, not by registers held across the step
       uint32_t ra[4], rb[8], cbits[2][4];
       int sl = lane;
       asm volatile("" : "+v"(sl));
