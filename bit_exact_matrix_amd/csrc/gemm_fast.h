@@ -792,6 +792,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
     };
   };
   for (int64_t s = 0; s < nsteps; s += 2) {
+    step_priority(s);
     if (s + 1 < nsteps) begin_fill(&stage1, s + 1);
     tile_step<MODEL, DT>(&stage0, ty, tx, X, NE, Xn, NEn, redo_at(s0 + s));
     if (s + 1 < nsteps) end_fill(&stage1);
@@ -807,6 +808,7 @@ __global__ __launch_bounds__(NT, (kWavesPerSimd<MODEL, DMA>)) void gemm_fast_ker
         for (int c = 0; c < 4; ++c) NE[q][c] = NEn[q][c];
       break;
     }
+    step_priority(s + 1);
     if (s + 2 < nsteps) begin_fill(&stage0, s + 2);
     tile_step<MODEL, DT>(&stage1, ty, tx, Xn, NEn, X, NE, redo_at(s0 + s + 1));
     if (s + 2 < nsteps) end_fill(&stage0);

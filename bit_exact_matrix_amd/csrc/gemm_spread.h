@@ -34,6 +34,7 @@ using narrowk::copy16_to_lds;  // the stages' global->LDS copies
 constexpr int IW = 40;   // words of one row's (column's) image at one position
 constexpr int TC = 16;   // tile columns; tile rows TR<L> = 16 / L
 constexpr int NSTAGE = 8;  // LDS stages: positions in flight
+static_assert(NSTAGE % 4 == 0, "a pass of stages starts at a position that is 0 mod 4");
 template <int L>
 constexpr int TR = 16 / L;
 
@@ -347,6 +348,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
         __builtin_amdgcn_s_waitcnt(kWaitAllButLast2);
         stage_barrier();
         copy(stage((u + NSTAGE - 1) % NSTAGE), t0 + u + NSTAGE - 1);
+        step_priority(u);  // t0 is a multiple of 4
         step(stage(u), t0 + u);
       }
     }
@@ -355,6 +357,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void g
       if (nfull + u < ns) {
         __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
         stage_barrier();
+        step_priority(u);
         step(stage(u), nfull + u);
       }
     }

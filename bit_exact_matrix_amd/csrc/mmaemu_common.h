@@ -258,6 +258,25 @@ __device__ __forceinline__ uint32_t load_code(const void* p, int64_t idx) {
   return ((const uint16_t*)p)[idx];
 }
 
+// Wave priority by chain position: 3, 2, 1, 0 for positions 0, 1, 2, 3
+// (mod 4).  The SIMD issues from the highest priority first, then from the
+// oldest wave.  With age alone, the oldest of the workgroups that share a
+// CU runs its chain almost as fast as a lone workgroup, and the others
+// catch up only after it ends, alone on their SIMDs, where a single wave
+// issues about half the time (measured on 512 x 4096 x 4096: the two
+// workgroups of a CU ended 1022 and 1741 us into the launch).  Cycling the
+// priority with the position makes a workgroup that is ahead yield to one
+// that is behind in most alignments of their positions, so that the chains
+// advance and end together.  It orders issue only: no result depends on it.
+__device__ __forceinline__ void step_priority(int64_t pos) {
+  switch (pos & 3) {
+    case 0: __builtin_amdgcn_s_setprio(3); break;
+    case 1: __builtin_amdgcn_s_setprio(2); break;
+    case 2: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 // x from the lane whose index differs in bit 0: a DPP quad permutation
 // [1, 0, 3, 2], a VALU move that needs every lane of the wave active.
 __device__ __forceinline__ uint32_t from_lane_xor1(uint32_t x) {
