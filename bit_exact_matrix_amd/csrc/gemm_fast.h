@@ -116,6 +116,21 @@ __device__ __forceinline__ uint32_t ffbh_into_hi(uint32_t packed, uint32_t x) {
       : "v"(x));
   return packed;
 }
+// v_ffbh_i32: the count of leading bits equal to the sign bit, 0xFFFFFFFF
+// for x = 0 (and -1).  For x = |S| ^ s (s = 0 or -1, S != -2^31) that is the
+// leading zeros of |S|: the bits of ~|S| above |S|'s leading one are ones.
+__device__ __forceinline__ uint32_t ffbh_i32(int x) {
+  uint32_t r;
+  asm("v_ffbh_i32 %0, %1" : "=v"(r) : "v"(x));
+  return r;
+}
+// The same count for x into the high word of packed (0xFFFF for x = 0).
+__device__ __forceinline__ uint32_t ffbh_i32_into_hi(uint32_t packed, int x) {
+  asm("v_ffbh_i32_sdwa %0, %1 dst_sel:WORD_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD"
+      : "+v"(packed)
+      : "v"(x));
+  return packed;
+}
 // Minimum of three pairs of 16-bit exponent codes.  Every code that reaches
 // it is a positive normal binary16 bit pattern (0x0800 .. 0x6000), and for
 // those the binary16 order is the integer order, so the packed binary16
@@ -581,16 +596,38 @@ __device__ __forceinline__ void group(const ST* st, int ty, int tx, int p0, int 
 // grid) and their exponent codes L = emax - F + 31 - lz, i.e.
 // NE = mn + (F - 31) + lz, by a saturating add so that a zero sum (lz all
 // ones) gets 0xFFFF.
+// Without an absolute value: U = S + s is |S| ^ s, the one's complement form
+// the result takes anyway.  Its signed leading-bit count is |S|'s leading
+// zeros lz, and a funnel shift of the pair (U, s) right by 32 - lz gives
+// (|S| << lz) ^ s, shifting in copies of the sign.  A second funnel shift of
+// (s, that) right by 8 keeps the 24 bits from the leading one down, the
+// magnitude cut toward zero, with the sign filled in above them.  A zero
+// sum has U = s = 0 and gives 0 whatever lz is.
 template <int EXTRA, int F>
 __device__ __forceinline__ void normalise2(int S0, int S1, uint32_t mn, int& X0, int& X1,
                                            uint32_t& NE) {
+  if constexpr (EXTRA != 0) {
+    // Hopper's final sum, moved up by EXTRA onto the 25-bit grid: the shift
+    // form compiles to v_lshlrev, v_lshrrev and one v_bitop3 per output,
+    // as short as the funnel form with its extra bits.
+    const int s0 = S0 >> 31, s1 = S1 >> 31;
+    const uint32_t m0 = (uint32_t)max(S0, -S0), m1 = (uint32_t)max(S1, -S1);
+    const uint32_t lz = ffbh_into_hi(ffbh(m0), m1);
+    X0 = (int)(((m0 << (lz & 31)) >> 8) << EXTRA) ^ s0;
+    X1 = (int)(((m1 << ((lz >> 16) & 31)) >> 8) << EXTRA) ^ s1;
+    const u16x2 base = as2(mn) - u16x2{(unsigned short)(31 - F), (unsigned short)(31 - F)};
+    NE = as32(__builtin_elementwise_add_sat(as2(lz), base));
+    return;
+  }
   const int s0 = S0 >> 31, s1 = S1 >> 31;
-  const uint32_t m0 = (uint32_t)max(S0, -S0), m1 = (uint32_t)max(S1, -S1);
-  // lz = lz0 | lz1 << 16; a shift reads the low 5 bits of its amount, so
-  // lz serves as lz0 as it stands and as lz1 through a high-word select
-  const uint32_t lz = ffbh_into_hi(ffbh(m0), m1);
-  X0 = (int)(((m0 << (lz & 31)) >> 8) << EXTRA) ^ s0;
-  X1 = (int)(((m1 << ((lz >> 16) & 31)) >> 8) << EXTRA) ^ s1;
+  const int U0 = S0 + s0, U1 = S1 + s1;
+  // lz = lz0 | lz1 << 16; a funnel shift reads the low 5 bits of its amount
+  const uint32_t lz = ffbh_i32_into_hi(ffbh_i32(U0), U1);
+  const uint32_t nlz = as32(u16x2{32, 32} - as2(lz));
+  const uint32_t W0 = __builtin_amdgcn_alignbit((uint32_t)U0, (uint32_t)s0, nlz);
+  const uint32_t W1 = __builtin_amdgcn_alignbit((uint32_t)U1, (uint32_t)s1, nlz >> 16);
+  X0 = (int)__builtin_amdgcn_alignbit((uint32_t)s0, W0, 8);
+  X1 = (int)__builtin_amdgcn_alignbit((uint32_t)s1, W1, 8);
   const u16x2 base = as2(mn) - u16x2{(unsigned short)(31 - F), (unsigned short)(31 - F)};
   NE = as32(__builtin_elementwise_add_sat(as2(lz), base));
 }
