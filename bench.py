@@ -229,6 +229,8 @@ def bench_shape(args):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    if args.copy_calibration:
+        copy_calibration(dev)
     got = D.cpu().numpy().view(np.uint32)
     ok = True
     for r in sorted({0, M // 2, M - 1}):
