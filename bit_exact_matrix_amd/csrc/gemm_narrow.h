@@ -119,13 +119,24 @@ __device__ __forceinline__ int group1(const uint32_t (&av)[16], const int (&as)[
 }
 
 // Normalise one group sum: one's complement significand (shifted by EXTRA
-// onto the next grid) and its exponent code, 0xFFFF for a zero sum.
+// onto the next grid) and its exponent code, 0xFFFF for a zero sum.  For
+// EXTRA = 0 by funnel shifts, as normalise2 in gemm_fast.h: U = S + s is
+// |S| ^ s, v_ffbh_i32 of U is |S|'s leading-zero count, and two
+// v_alignbit_b32 cut the 24 bits below it in one's complement form.
 template <int EXTRA, int F>
 __device__ __forceinline__ void normalise1(int S, uint32_t mn, int& X, uint32_t& NE) {
   const int s = S >> 31;
-  const uint32_t m = (uint32_t)max(S, -S);
-  const uint32_t lz = ffbh(m);
-  X = (int)(((m << (lz & 31)) >> 8) << EXTRA) ^ s;
+  uint32_t lz;
+  if constexpr (EXTRA == 0) {
+    const int U = S + s;
+    lz = ffbh_i32(U);
+    const uint32_t W = __builtin_amdgcn_alignbit((uint32_t)U, (uint32_t)s, 32u - lz);
+    X = (int)__builtin_amdgcn_alignbit((uint32_t)s, W, 8);
+  } else {
+    const uint32_t m = (uint32_t)max(S, -S);
+    lz = ffbh(m);
+    X = (int)(((m << (lz & 31)) >> 8) << EXTRA) ^ s;
+  }
   const u16x2 base = splat_lo(mn) - u16x2{(unsigned short)(31 - F), (unsigned short)(31 - F)};
   NE = as32(__builtin_elementwise_add_sat(splat_lo(lz), base)) & 0xFFFFu;
 }
